@@ -1,0 +1,127 @@
+"""ctypes binding of the plain CPU oracle (``oracle/oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the product path.  It shares no code
+with the HIP library; both are fed the same seeded inputs from ``synthetic``.
+
+Every function here is argument marshalling around the C file, which states
+the definition it follows (the paged FP8 indexer of the sglang pull request
+page "sgl-project/sglang#48224", sgl-amd-mono #86 commit body).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (fp64, -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math",
+                               "-ffp-contract=off", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        I = ctypes.c_int
+        lib.oracle_e4m3_decode.restype = ctypes.c_double
+        lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_bf16_decode.restype = ctypes.c_double
+        lib.oracle_bf16_decode.argtypes = [ctypes.c_uint16]
+        lib.oracle_score_range.restype = I
+        lib.oracle_score_range.argtypes = [I, I64, I64, P, P, P, P, I, P, I, I, P, P, P, P]
+        lib.oracle_score_samples.restype = I
+        lib.oracle_score_samples.argtypes = [I64, P, P, P, P, P, P, I, P, I, I, P, P, P, P]
+        lib.oracle_topk_f32.restype = I
+        lib.oracle_topk_f32.argtypes = [P, I64, I, P]
+        lib.oracle_topk_f64.restype = I
+        lib.oracle_topk_f64.argtypes = [P, I64, I, P]
+        _lib = lib
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def e4m3_decode(code: int) -> float:
+    return float(_load().oracle_e4m3_decode(int(code) & 0xFF))
+
+
+def bf16_decode(bits: int) -> float:
+    return float(_load().oracle_bf16_decode(int(bits) & 0xFFFF))
+
+
+def _arrays(p):
+    return (np.ascontiguousarray(p.q_bf16, dtype=np.uint16),
+            np.ascontiguousarray(p.w, dtype=np.float32),
+            np.ascontiguousarray(p.k_e4m3, dtype=np.uint8),
+            np.ascontiguousarray(p.k_scale, dtype=np.float32),
+            np.ascontiguousarray(p.page_table, dtype=np.int32),
+            np.ascontiguousarray(p.row_pt, dtype=np.int32),
+            np.ascontiguousarray(p.row_bound, dtype=np.int32))
+
+
+def score_range(p, r: int, s0: int = 0, s1: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """fp64 scores and tolerance scales of row r for keys [s0, s1) ∩ [0, bound)."""
+    q, w, k8, ks, pt, rp, rb = _arrays(p)
+    b = int(rb[r])
+    s1 = b if s1 is None else min(int(s1), b)
+    n = max(0, s1 - s0)
+    sc = np.empty(max(n, 1), dtype=np.float64)
+    bd = np.empty(max(n, 1), dtype=np.float64)
+    rc = _load().oracle_score_range(int(r), int(s0), int(s1), _p(q), _p(w), _p(k8), _p(ks),
+                                    int(k8.shape[0]), _p(pt), int(pt.shape[0]), int(pt.shape[1]),
+                                    _p(rp), _p(rb), _p(sc), _p(bd))
+    if rc != 0:
+        raise RuntimeError(f"oracle_score_range failed: {rc}")
+    return sc[:n], bd[:n]
+
+
+def score_samples(p, rows: np.ndarray, keys: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """fp64 scores and tolerance scales for explicit (row, key) samples."""
+    q, w, k8, ks, pt, rp, rb = _arrays(p)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    keys = np.ascontiguousarray(keys, dtype=np.int64)
+    n = rows.size
+    sc = np.empty(max(n, 1), dtype=np.float64)
+    bd = np.empty(max(n, 1), dtype=np.float64)
+    rc = _load().oracle_score_samples(int(n), _p(rows), _p(keys), _p(q), _p(w), _p(k8), _p(ks),
+                                      int(k8.shape[0]), _p(pt), int(pt.shape[0]), int(pt.shape[1]),
+                                      _p(rp), _p(rb), _p(sc), _p(bd))
+    if rc != 0:
+        raise RuntimeError(f"oracle_score_samples failed: {rc}")
+    return sc[:n], bd[:n]
+
+
+def topk(scores: np.ndarray, k: int) -> np.ndarray:
+    """Exact top-k of one row (fp32 or fp64 values), ties to the lower index,
+    NaN last; returns int32[k] padded with -1 (order: selection order)."""
+    out = np.empty(k, dtype=np.int32)
+    if scores.dtype == np.float32:
+        a = np.ascontiguousarray(scores)
+        rc = _load().oracle_topk_f32(_p(a), int(a.size), int(k), _p(out))
+    else:
+        a = np.ascontiguousarray(scores, dtype=np.float64)
+        rc = _load().oracle_topk_f64(_p(a), int(a.size), int(k), _p(out))
+    if rc != 0:
+        raise RuntimeError(f"oracle_topk failed: {rc}")
+    return out

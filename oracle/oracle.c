@@ -1,0 +1,242 @@
+/*
+ * Plain CPU oracle for the paged FP8-E4M3 decode indexer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or calls
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg do.  It shares no code, header or table with the HIP library.
+ *
+ * What it computes (the indexer launch of the sglang pull request page
+ * "sgl-project/sglang#48224", sgl-amd-mono #86 commit body, Motivation: every
+ * cached key of each row is scored, then each row's exact top-k is selected):
+ *
+ *   for row r and logical key s < bound[r]:
+ *     p = page_table[row_pt[r]][s / 64], o = s % 64
+ *     d_h   = sum_{i<128} q[r][h][i] * dec(k8[p][o][i])          (fp64, i order)
+ *     score = scale[p][o] * sum_{h<64} w[r][h] * max(d_h, 0)
+ *     bnd   = scale[p][o] * sum_{h<64} |w[r][h]| * |d_h|          (tolerance scale)
+ *
+ * Keys at or past a row's bound are not scored (same page, #86 commit 2: the
+ * store's mask drops keys at or past the row's bound, so the bound is
+ * exclusive).  Top-k: descending by value, ties to the lower key index, NaN
+ * below every number, -0 equal to +0; the first min(k, bound) of that order,
+ * padded with -1.  The selection is a plain full sort (qsort) of all
+ * (value, index) pairs.
+ *
+ * Plain C, fp64, one thread, no intrinsics.  Build: gcc -O2 -fPIC -shared
+ * (no -ffast-math, so no floating-point reassociation).
+ *
+ * Return codes: 0 ok, -1 invalid argument, -2 page id / page-table row out of
+ * range (nothing is read out of bounds).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_H 64
+#define ORC_D 128
+#define ORC_PAGE 64
+
+/* OCP 8-bit floating point, E4M3 ("FN": no infinities, S.1111.111 is NaN):
+ * exponent bias 7; exponent field 0 is subnormal (m/8) * 2^-6. */
+double oracle_e4m3_decode(uint8_t b)
+{
+    int s = (b >> 7) & 1;
+    int e = (b >> 3) & 15;
+    int m = b & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* bfloat16: the upper 16 bits of an IEEE binary32. */
+double oracle_bf16_decode(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* One key-row: score and tolerance scale.  Returns 0, or -2 if the page
+ * lookup is out of range. */
+static int score_one(const uint16_t *q_r, const float *w_r, const uint8_t *k8,
+                     const float *kscale, int num_pages, const int32_t *pt_row,
+                     int64_t s, double *score, double *bnd)
+{
+    int32_t page = pt_row[s / ORC_PAGE];
+    int64_t slot = s % ORC_PAGE;
+    const uint8_t *key;
+    double kv[ORC_D];
+    double c, acc = 0.0, accb = 0.0;
+    int h, i;
+    if (page < 0 || page >= num_pages)
+        return -2;
+    key = k8 + ((int64_t)page * ORC_PAGE + slot) * ORC_D;
+    c = (double)kscale[(int64_t)page * ORC_PAGE + slot];
+    for (i = 0; i < ORC_D; ++i)
+        kv[i] = oracle_e4m3_decode(key[i]);
+    for (h = 0; h < ORC_H; ++h) {
+        double d = 0.0;
+        for (i = 0; i < ORC_D; ++i)
+            d += oracle_bf16_decode(q_r[h * ORC_D + i]) * kv[i];
+        acc += (double)w_r[h] * (d > 0.0 ? d : 0.0);
+        accb += fabs((double)w_r[h]) * fabs(d);
+    }
+    *score = c * acc;
+    *bnd = c * accb;
+    return 0;
+}
+
+/* Scores of row r for keys s in [s0, s1) (clipped to the row's bound).
+ * q: [rows][64][128] bf16 bits; w: [rows][64]; k8: [num_pages][64][128];
+ * kscale: [num_pages][64]; page_table: [pt_rows][pt_stride].
+ * out_score[s - s0], out_bnd[s - s0] (out_bnd may be NULL). */
+int oracle_score_range(int r, int64_t s0, int64_t s1,
+                       const uint16_t *q, const float *w,
+                       const uint8_t *k8, const float *kscale, int num_pages,
+                       const int32_t *page_table, int pt_rows, int pt_stride,
+                       const int32_t *row_pt, const int32_t *row_bound,
+                       double *out_score, double *out_bnd)
+{
+    int64_t s, b;
+    int pr;
+    if (!q || !w || !k8 || !kscale || !page_table || !row_pt || !row_bound || !out_score)
+        return -1;
+    if (r < 0 || s0 < 0 || s1 < s0)
+        return -1;
+    pr = row_pt[r];
+    if (pr < 0 || pr >= pt_rows)
+        return -2;
+    b = row_bound[r];
+    if (b > (int64_t)pt_stride * ORC_PAGE)
+        return -1;
+    if (s1 > b)
+        s1 = b;
+    for (s = s0; s < s1; ++s) {
+        double sc, bd;
+        int rc = score_one(q + (int64_t)r * ORC_H * ORC_D, w + (int64_t)r * ORC_H, k8,
+                           kscale, num_pages, page_table + (int64_t)pr * pt_stride, s,
+                           &sc, &bd);
+        if (rc)
+            return rc;
+        out_score[s - s0] = sc;
+        if (out_bnd)
+            out_bnd[s - s0] = bd;
+    }
+    return 0;
+}
+
+/* Scores for an explicit list of (row, key) samples. */
+int oracle_score_samples(int64_t nsamp, const int32_t *samp_row, const int64_t *samp_key,
+                         const uint16_t *q, const float *w,
+                         const uint8_t *k8, const float *kscale, int num_pages,
+                         const int32_t *page_table, int pt_rows, int pt_stride,
+                         const int32_t *row_pt, const int32_t *row_bound,
+                         double *out_score, double *out_bnd)
+{
+    int64_t i;
+    for (i = 0; i < nsamp; ++i) {
+        int r = samp_row[i];
+        int64_t s = samp_key[i];
+        int pr = row_pt[r];
+        double sc, bd;
+        int rc;
+        if (pr < 0 || pr >= pt_rows)
+            return -2;
+        if (s < 0 || s >= row_bound[r] || s >= (int64_t)pt_stride * ORC_PAGE)
+            return -1;
+        rc = score_one(q + (int64_t)r * ORC_H * ORC_D, w + (int64_t)r * ORC_H, k8, kscale,
+                       num_pages, page_table + (int64_t)pr * pt_stride, s, &sc, &bd);
+        if (rc)
+            return rc;
+        out_score[i] = sc;
+        if (out_bnd)
+            out_bnd[i] = bd;
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------- top-k */
+
+typedef struct {
+    double v;
+    int64_t i;
+} orc_pair;
+
+/* "a comes before b": larger value first; NaN after every number; equal
+ * values (and -0 vs +0, and NaN vs NaN) by lower index. */
+static int before(const orc_pair *a, const orc_pair *b)
+{
+    int an = isnan(a->v), bn = isnan(b->v);
+    if (an != bn)
+        return bn;                  /* the number comes first */
+    if (!an && a->v != b->v)
+        return a->v > b->v;
+    return a->i < b->i;
+}
+
+static int cmp_pair(const void *pa, const void *pb)
+{
+    const orc_pair *a = (const orc_pair *)pa, *b = (const orc_pair *)pb;
+    if (before(a, b))
+        return -1;
+    if (before(b, a))
+        return 1;
+    return 0;
+}
+
+static int topk_pairs(orc_pair *pr, int64_t n, int k, int32_t *out)
+{
+    int64_t i, take;
+    qsort(pr, (size_t)n, sizeof *pr, cmp_pair);
+    take = n < k ? n : k;
+    for (i = 0; i < take; ++i)
+        out[i] = (int32_t)pr[i].i;
+    for (i = take; i < k; ++i)
+        out[i] = -1;
+    return 0;
+}
+
+/* Top-k of scores[0..n) given as fp32 (the GPU's own scores). */
+int oracle_topk_f32(const float *scores, int64_t n, int k, int32_t *out)
+{
+    orc_pair *pr;
+    int64_t i;
+    if (n < 0 || k < 1 || !out || (n > 0 && !scores))
+        return -1;
+    pr = (orc_pair *)malloc(sizeof(orc_pair) * (size_t)(n > 0 ? n : 1));
+    if (!pr)
+        return -1;
+    for (i = 0; i < n; ++i) {
+        pr[i].v = (double)scores[i];
+        pr[i].i = i;
+    }
+    topk_pairs(pr, n, k, out);
+    free(pr);
+    return 0;
+}
+
+/* Top-k of scores[0..n) given in fp64 (the oracle's own scores). */
+int oracle_topk_f64(const double *scores, int64_t n, int k, int32_t *out)
+{
+    orc_pair *pr;
+    int64_t i;
+    if (n < 0 || k < 1 || !out || (n > 0 && !scores))
+        return -1;
+    pr = (orc_pair *)malloc(sizeof(orc_pair) * (size_t)(n > 0 ? n : 1));
+    if (!pr)
+        return -1;
+    for (i = 0; i < n; ++i) {
+        pr[i].v = scores[i];
+        pr[i].i = i;
+    }
+    topk_pairs(pr, n, k, out);
+    free(pr);
+    return 0;
+}
