@@ -1,0 +1,184 @@
+"""Python binding of libfp8idx, the MI355X (gfx950) paged FP8 decode indexer.
+
+Argument marshalling only: every step (scoring, masking, first-digit counting,
+selection) runs in the HIP kernels behind the C ABI declared in
+``include/fp8idx.h``.  PyTorch is used for device memory and the current
+stream.  If the compiled library is missing the import of any entry point
+raises; there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfp8idx.so")
+
+HEADS = 64
+HEAD_DIM = 128
+PAGE = 64
+MAX_TOPK = 2048
+
+EXPORTED = ("fp8idx_abi_version", "fp8idx_strerror", "fp8idx_workspace_size",
+            "fp8idx_workspace_init", "indexer_score", "indexer_topk", "indexer_launch")
+
+
+class Problem(ctypes.Structure):
+    """Mirror of fp8idx_problem_t."""
+    _fields_ = [("rows", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("pt_rows", ctypes.c_int32), ("pt_stride", ctypes.c_int32),
+                ("max_bound", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("score_stride", ctypes.c_int64)]
+
+
+class Fp8IdxError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"fp8idx error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the compiled library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with fp8_key_scoring_amd/build.py "
+                          "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.fp8idx_abi_version.restype = ctypes.c_int
+    lib.fp8idx_abi_version.argtypes = []
+    lib.fp8idx_strerror.restype = ctypes.c_char_p
+    lib.fp8idx_strerror.argtypes = [ctypes.c_int]
+    lib.fp8idx_workspace_size.restype = ctypes.c_int
+    lib.fp8idx_workspace_size.argtypes = [ctypes.POINTER(Problem), ctypes.c_int,
+                                          ctypes.POINTER(ctypes.c_size_t)]
+    lib.fp8idx_workspace_init.restype = ctypes.c_int
+    lib.fp8idx_workspace_init.argtypes = [P, ctypes.c_size_t, P]
+    lib.indexer_score.restype = ctypes.c_int
+    lib.indexer_score.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, P]
+    lib.indexer_topk.restype = ctypes.c_int
+    lib.indexer_topk.argtypes = [ctypes.POINTER(Problem), P, P, P, P, ctypes.c_size_t, P]
+    lib.indexer_launch.restype = ctypes.c_int
+    lib.indexer_launch.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, P, P,
+                                   ctypes.c_size_t, P]
+    _lib = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        msg = load_library().fp8idx_strerror(rc).decode()
+        raise Fp8IdxError(rc, msg)
+
+
+def abi_version() -> int:
+    return int(load_library().fp8idx_abi_version())
+
+
+def make_problem(rows: int, num_pages: int, pt_rows: int, pt_stride: int, max_bound: int,
+                 topk: int = MAX_TOPK, score_stride: int = 0) -> Problem:
+    return Problem(rows, num_pages, pt_rows, pt_stride, max_bound, topk, score_stride)
+
+
+def workspace_size(prob: Problem, scores_in_workspace: bool) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().fp8idx_workspace_size(ctypes.byref(prob), int(bool(scores_in_workspace)),
+                                                ctypes.byref(n)))
+    return int(n.value)
+
+
+def _stream(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def new_workspace(prob: Problem, scores_in_workspace: bool, device):
+    """A zero-filled workspace tensor (uint8, 256-byte aligned base)."""
+    import torch
+    n = workspace_size(prob, scores_in_workspace)
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    ws = ws[off:off + n]
+    _check(load_library().fp8idx_workspace_init(ws.data_ptr(), n, _stream(ws.device)))
+    return ws
+
+
+def _problem_from(q, k_e4m3, page_table, max_bound: int, topk: int, score_stride: int) -> Problem:
+    return make_problem(rows=q.shape[0], num_pages=k_e4m3.shape[0], pt_rows=page_table.shape[0],
+                        pt_stride=page_table.shape[1], max_bound=max_bound, topk=topk,
+                        score_stride=score_stride)
+
+
+def _check_inputs(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound):
+    import torch
+    R = q.shape[0]
+    assert q.dtype == torch.bfloat16 and tuple(q.shape[1:]) == (HEADS, HEAD_DIM) and q.is_contiguous()
+    assert w.dtype == torch.float32 and tuple(w.shape) == (R, HEADS) and w.is_contiguous()
+    assert k_e4m3.dtype == torch.uint8 and tuple(k_e4m3.shape[1:]) == (PAGE, HEAD_DIM) and k_e4m3.is_contiguous()
+    assert k_scale.dtype == torch.float32 and tuple(k_scale.shape) == (k_e4m3.shape[0], PAGE) and k_scale.is_contiguous()
+    assert page_table.dtype == torch.int32 and page_table.dim() == 2 and page_table.is_contiguous()
+    assert row_pt.dtype == torch.int32 and tuple(row_pt.shape) == (R,) and row_pt.is_contiguous()
+    assert row_bound.dtype == torch.int32 and tuple(row_bound.shape) == (R,) and row_bound.is_contiguous()
+
+
+def indexer_score(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound, *, max_bound: int,
+                  scores=None):
+    """Scores [rows, score_stride] fp32; entries at or past a row's bound untouched."""
+    import torch
+    _check_inputs(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound)
+    if scores is None:
+        scores = torch.full((q.shape[0], max(1, max_bound)), float("nan"), dtype=torch.float32,
+                            device=q.device)
+    assert scores.dtype == torch.float32 and scores.dim() == 2 and scores.stride(1) == 1
+    prob = _problem_from(q, k_e4m3, page_table, max_bound, MAX_TOPK, scores.stride(0))
+    _check(load_library().indexer_score(ctypes.byref(prob), _ptr(q), _ptr(w), _ptr(k_e4m3),
+                                        _ptr(k_scale), _ptr(page_table), _ptr(row_pt),
+                                        _ptr(row_bound), _ptr(scores), _stream(q.device)))
+    return scores
+
+
+def indexer_topk(scores, row_bound, *, max_bound: int, topk: int = MAX_TOPK, out_idx=None,
+                 workspace=None):
+    """Exact top-k indices [rows, topk] int32 (ascending index order, -1 padded)."""
+    import torch
+    assert scores.dtype == torch.float32 and scores.dim() == 2 and scores.stride(1) == 1
+    R = scores.shape[0]
+    prob = make_problem(rows=R, num_pages=1, pt_rows=1, pt_stride=max(1, (max_bound + 63) // 64),
+                        max_bound=max_bound, topk=topk, score_stride=scores.stride(0))
+    if out_idx is None:
+        out_idx = torch.empty((R, topk), dtype=torch.int32, device=scores.device)
+    if workspace is None:
+        workspace = new_workspace(prob, False, scores.device)
+    _check(load_library().indexer_topk(ctypes.byref(prob), _ptr(scores), _ptr(row_bound),
+                                       _ptr(out_idx), _ptr(workspace), workspace.numel(),
+                                       _stream(scores.device)))
+    return out_idx
+
+
+def indexer_launch(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound, *, max_bound: int,
+                   topk: int = MAX_TOPK, scores=None, out_idx=None, workspace=None):
+    """Fused scoring + exact top-k.  Returns out_idx [rows, topk] int32."""
+    import torch
+    _check_inputs(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound)
+    R = q.shape[0]
+    sstride = scores.stride(0) if scores is not None else 0
+    prob = _problem_from(q, k_e4m3, page_table, max_bound, topk, sstride)
+    if out_idx is None:
+        out_idx = torch.empty((R, topk), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(prob, scores is None, q.device)
+    _check(load_library().indexer_launch(ctypes.byref(prob), _ptr(q), _ptr(w), _ptr(k_e4m3),
+                                         _ptr(k_scale), _ptr(page_table), _ptr(row_pt),
+                                         _ptr(row_bound), _ptr(scores), _ptr(out_idx),
+                                         _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return out_idx

@@ -1,0 +1,197 @@
+// C ABI of libfp8idx (declared in include/fp8idx.h): host-side argument
+// checks, workspace layout and the kernel launch sequence.  Everything is
+// enqueued on the caller's stream; nothing is allocated or synchronised.
+#include "fp8idx.h"
+#include "common.h"
+
+#include <atomic>
+#include <cstring>
+
+using namespace fp8idx;
+
+namespace {
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_problem(const fp8idx_problem_t *p) {
+    if (!p) return FP8IDX_EINVAL;
+    if (p->rows < 1 || p->rows > 65535) return FP8IDX_EINVAL;
+    if (p->topk < 1 || p->topk > FP8IDX_MAX_TOPK) return FP8IDX_EINVAL;
+    if (p->max_bound < 0) return FP8IDX_EINVAL;
+    return FP8IDX_OK;
+}
+
+int check_score_inputs(const fp8idx_problem_t *p, const void *q, const float *w,
+                       const uint8_t *k8, const float *ks, const int32_t *pt,
+                       const int32_t *row_pt, const int32_t *row_bound) {
+    if (p->num_pages < 1 || p->pt_rows < 1 || p->pt_stride < 1) return FP8IDX_EINVAL;
+    if ((int64_t)p->max_bound > (int64_t)p->pt_stride * FP8IDX_PAGE) return FP8IDX_EINVAL;
+    if (!q || !w || !k8 || !ks || !pt || !row_pt || !row_bound) return FP8IDX_EINVAL;
+    if (!aligned(q, 16) || !aligned(w, 16) || !aligned(k8, 16) || !aligned(ks, 4) ||
+        !aligned(pt, 4) || !aligned(row_pt, 4) || !aligned(row_bound, 4))
+        return FP8IDX_EINVAL;
+    return FP8IDX_OK;
+}
+
+// gfx950 check, cached per device id.
+std::atomic<int> g_dev_ok[64];
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FP8IDX_EDEVICE;
+    if (dev < 64) {
+        int c = g_dev_ok[dev].load(std::memory_order_relaxed);
+        if (c == 1) return FP8IDX_OK;
+        if (c == 2) return FP8IDX_EDEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8IDX_EDEVICE;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) g_dev_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? FP8IDX_OK : FP8IDX_EDEVICE;
+}
+
+int score_chunk(const fp8idx_problem_t *p) {
+    // aim at about two workgroups per CU on the longest request group
+    const int64_t groups = (p->rows + kGroupRows - 1) / kGroupRows;
+    int64_t ch = groups * (int64_t)p->max_bound / 512;
+    ch = (ch + 63) / 64 * 64;
+    if (ch < 256) ch = 256;
+    if (ch > 8192) ch = 8192;
+    return (int)ch;
+}
+
+ScoreArgs make_score_args(const fp8idx_problem_t *p, const void *q, const float *w,
+                          const uint8_t *k8, const float *ks, const int32_t *pt,
+                          const int32_t *row_pt, const int32_t *row_bound, float *scores,
+                          int64_t sstride, uint32_t *hist1) {
+    ScoreArgs a;
+    a.q = (const uint16_t *)q;
+    a.w = w;
+    a.k8 = k8;
+    a.kscale = ks;
+    a.page_table = pt;
+    a.row_pt = row_pt;
+    a.row_bound = row_bound;
+    a.scores = scores;
+    a.hist1 = hist1;
+    a.sstride = sstride;
+    a.rows = p->rows;
+    a.num_pages = p->num_pages;
+    a.pt_rows = p->pt_rows;
+    a.pt_stride = p->pt_stride;
+    a.max_bound = p->max_bound;
+    a.chunk = score_chunk(p);
+    return a;
+}
+
+int to_code(hipError_t e) { return e == hipSuccess ? FP8IDX_OK : FP8IDX_ELAUNCH; }
+
+int run_select(const fp8idx_problem_t *p, const float *scores, int64_t sstride,
+               const int32_t *row_bound, int32_t *out_idx, unsigned char *ws,
+               const WsLayout &L, bool need_hist1, hipStream_t st) {
+    SelectArgs a;
+    a.scores = scores;
+    a.row_bound = row_bound;
+    a.out_idx = out_idx;
+    a.ws = ws;
+    a.L = L;
+    a.sstride = sstride;
+    a.rows = p->rows;
+    a.max_bound = p->max_bound;
+    a.topk = p->topk;
+    hipError_t e = hipSuccess;
+    if (need_hist1 && (e = launch_hist1(a, st)) != hipSuccess) return to_code(e);
+    if ((e = launch_refine(a, st)) != hipSuccess) return to_code(e);
+    return to_code(launch_gather(a, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8idx_abi_version(void) { return FP8IDX_ABI_VERSION; }
+
+const char *fp8idx_strerror(int code) {
+    switch (code) {
+    case FP8IDX_OK: return "ok";
+    case FP8IDX_EINVAL: return "invalid argument";
+    case FP8IDX_EWORKSPACE: return "workspace missing or too small";
+    case FP8IDX_ELAUNCH: return "kernel launch failed";
+    case FP8IDX_EDEVICE: return "no gfx950 device is current";
+    default: return "unknown error";
+    }
+}
+
+int fp8idx_workspace_size(const fp8idx_problem_t *p, int scores_in_workspace, size_t *bytes) {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if (!bytes) return FP8IDX_EINVAL;
+    *bytes = ws_layout(p->rows, p->max_bound, scores_in_workspace != 0).total;
+    return FP8IDX_OK;
+}
+
+int fp8idx_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+    if (!ws || !aligned(ws, 256) || ws_bytes % 4) return FP8IDX_EINVAL;
+    int rc = check_device();
+    if (rc) return rc;
+    return to_code(launch_fill_zero(ws, ws_bytes, (hipStream_t)stream));
+}
+
+int indexer_score(const fp8idx_problem_t *p, const void *q_bf16, const float *w,
+                  const uint8_t *k_e4m3, const float *k_scale, const int32_t *page_table,
+                  const int32_t *row_pt, const int32_t *row_bound, float *scores,
+                  void *stream) {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    rc = check_score_inputs(p, q_bf16, w, k_e4m3, k_scale, page_table, row_pt, row_bound);
+    if (rc) return rc;
+    if (!scores || !aligned(scores, 4) || p->score_stride < p->max_bound) return FP8IDX_EINVAL;
+    rc = check_device();
+    if (rc) return rc;
+    ScoreArgs a = make_score_args(p, q_bf16, w, k_e4m3, k_scale, page_table, row_pt, row_bound,
+                                  scores, p->score_stride, nullptr);
+    return to_code(launch_score(a, (hipStream_t)stream));
+}
+
+int indexer_topk(const fp8idx_problem_t *p, const float *scores, const int32_t *row_bound,
+                 int32_t *out_idx, void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if (!scores || !row_bound || !out_idx) return FP8IDX_EINVAL;
+    if (!aligned(scores, 4) || !aligned(row_bound, 4) || !aligned(out_idx, 4)) return FP8IDX_EINVAL;
+    if (p->score_stride < p->max_bound) return FP8IDX_EINVAL;
+    const WsLayout L = ws_layout(p->rows, p->max_bound, false);
+    if (!ws || !aligned(ws, 256) || ws_bytes < L.total) return FP8IDX_EWORKSPACE;
+    rc = check_device();
+    if (rc) return rc;
+    return run_select(p, scores, p->score_stride, row_bound, out_idx, (unsigned char *)ws, L,
+                      true, (hipStream_t)stream);
+}
+
+int indexer_launch(const fp8idx_problem_t *p, const void *q_bf16, const float *w,
+                   const uint8_t *k_e4m3, const float *k_scale, const int32_t *page_table,
+                   const int32_t *row_pt, const int32_t *row_bound, float *scores,
+                   int32_t *out_idx, void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    rc = check_score_inputs(p, q_bf16, w, k_e4m3, k_scale, page_table, row_pt, row_bound);
+    if (rc) return rc;
+    if (!out_idx || !aligned(out_idx, 4)) return FP8IDX_EINVAL;
+    if (scores && (!aligned(scores, 4) || p->score_stride < p->max_bound)) return FP8IDX_EINVAL;
+    const WsLayout L = ws_layout(p->rows, p->max_bound, scores == nullptr);
+    if (!ws || !aligned(ws, 256) || ws_bytes < L.total) return FP8IDX_EWORKSPACE;
+    rc = check_device();
+    if (rc) return rc;
+    unsigned char *wsb = (unsigned char *)ws;
+    float *sc = scores ? scores : (float *)(wsb + L.scores);
+    const int64_t sstride = scores ? p->score_stride : L.sstride;
+    hipStream_t st = (hipStream_t)stream;
+    ScoreArgs a = make_score_args(p, q_bf16, w, k_e4m3, k_scale, page_table, row_pt, row_bound,
+                                  sc, sstride, (uint32_t *)(wsb + L.hist1));
+    rc = to_code(launch_score(a, st));
+    if (rc) return rc;
+    return run_select(p, sc, sstride, row_bound, out_idx, wsb, L, false, st);
+}
+
+}  // extern "C"

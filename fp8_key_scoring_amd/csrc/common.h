@@ -1,0 +1,133 @@
+// Internal definitions shared by the HIP translation units of libfp8idx.
+// Not part of the public ABI (include/fp8idx.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8idx {
+
+constexpr int kHeads = 64;
+constexpr int kDim = 128;
+constexpr int kPage = 64;
+constexpr int kMaxTopk = 2048;
+
+// Scoring: one workgroup = 4 waves; up to 4 rows that share a page-table row
+// are scored together (one wave per row, each key read from HBM once).
+constexpr int kScoreThreads = 256;
+constexpr int kGroupRows = 4;
+constexpr int kKeysPerMfma = 16;   // one 16x16x32 MFMA column block = 16 keys
+
+// Selection.
+constexpr int kSelThreads = 256;
+constexpr int kSelChunkMin = 8192;  // keys per selection workgroup (at least)
+constexpr int kSelMaxWgs = 64;      // selection workgroups per row (at most)
+constexpr int kCandCap = 4096;      // candidates kept per row for the final sort
+constexpr int kZeroRows = 1024;    // rows the zero block is laid out for (at least)
+constexpr int kDigit1Bits = 6;      // first radix digit (counted while scoring)
+constexpr int kDigit2Bits = 8;      // second radix digit
+constexpr int kDigit1Shift = 32 - kDigit1Bits;               // 26
+constexpr int kDigit2Shift = kDigit1Shift - kDigit2Bits;     // 18
+constexpr int kBins1 = 1 << kDigit1Bits;                     // 64
+constexpr int kBins2 = 1 << kDigit2Bits;                     // 256
+
+// Per-row selection state, written by the last refine workgroup of a row.
+struct RowState {
+    uint32_t b1;      // first-digit bin holding the k-th largest key
+    uint32_t b2;      // second-digit bin inside b1 holding it
+    uint32_t sure;    // keys whose top 14 bits exceed (b1, b2): all selected
+    uint32_t need;    // keys still to take from the (b1, b2) bin
+    uint32_t cand;    // keys in the (b1, b2) bin
+    uint32_t pad[3];
+};
+
+// Workspace layout.  Counters and histograms must be zero before a launch;
+// every launch leaves them zero again.  They sit in one block at the start,
+// laid out for max(rows, kZeroRows) rows, so the block has the same offsets
+// for every problem of up to kZeroRows rows and a workspace can be reused
+// across problem shapes; the rest of the workspace is scratch.
+struct WsLayout {
+    size_t hist1;      // u32 [rows][64]
+    size_t cnt2;       // u32 [rows]   refine completion counters
+    size_t cnt3;       // u32 [rows]   gather completion counters
+    size_t sure_slot;  // u32 [rows]
+    size_t cand_slot;  // u32 [rows]
+    size_t state;      // RowState [rows]
+    size_t hist2p;     // u32 [rows][sel_wgs][256]   per-workgroup partials
+    size_t cand;       // u64 [rows][kCandCap]
+    size_t scores;     // f32 [rows][sstride]  (only when the caller gives none)
+    size_t total;
+    int sel_wgs;
+    int64_t sel_chunk;
+    int64_t sstride;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline WsLayout ws_layout(int rows, int max_bound, bool own_scores) {
+    WsLayout L{};
+    int64_t mb = max_bound > 0 ? max_bound : 1;
+    int s = (int)((mb + kSelChunkMin - 1) / kSelChunkMin);
+    if (s < 1) s = 1;
+    if (s > kSelMaxWgs) s = kSelMaxWgs;
+    L.sel_wgs = s;
+    int64_t ch = (mb + s - 1) / s;
+    L.sel_chunk = (ch + kSelThreads - 1) / kSelThreads * kSelThreads;
+    L.sstride = (int64_t)align_up((size_t)mb, 64);
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+    const size_t rz = (size_t)(rows > kZeroRows ? rows : kZeroRows);
+    L.hist1 = take(rz * kBins1 * 4);
+    L.cnt2 = take(rz * 4);
+    L.cnt3 = take(rz * 4);
+    L.sure_slot = take(rz * 4);
+    L.cand_slot = take(rz * 4);
+    L.state = take((size_t)rows * sizeof(RowState));
+    L.hist2p = take((size_t)rows * s * kBins2 * 4);
+    L.cand = take((size_t)rows * kCandCap * 8);
+    L.scores = own_scores ? take((size_t)rows * (size_t)L.sstride * 4) : off;
+    L.total = off;
+    return L;
+}
+
+// Order-preserving map fp32 -> u32 used as the radix key: larger float ->
+// larger key; -0 and +0 map to the same key; every NaN maps to 0, below -inf.
+__device__ __forceinline__ uint32_t radix_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    u = (u == 0x80000000u) ? 0u : u;
+    uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return (f != f) ? 0u : k;
+}
+
+struct ScoreArgs {
+    const uint16_t *q;
+    const float *w;
+    const uint8_t *k8;
+    const float *kscale;
+    const int32_t *page_table;
+    const int32_t *row_pt;
+    const int32_t *row_bound;
+    float *scores;
+    uint32_t *hist1;   // null: no first-digit counting
+    int64_t sstride;
+    int rows, num_pages, pt_rows, pt_stride, max_bound, chunk;
+};
+
+struct SelectArgs {
+    const float *scores;
+    const int32_t *row_bound;
+    int32_t *out_idx;
+    unsigned char *ws;
+    WsLayout L;
+    int64_t sstride;
+    int rows, max_bound, topk;
+};
+
+hipError_t launch_score(const ScoreArgs &a, hipStream_t st);
+hipError_t launch_hist1(const SelectArgs &a, hipStream_t st);
+hipError_t launch_refine(const SelectArgs &a, hipStream_t st);
+hipError_t launch_gather(const SelectArgs &a, hipStream_t st);
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
+
+}  // namespace fp8idx

@@ -1,0 +1,151 @@
+/*
+ * fp8idx — paged FP8-E4M3 decode indexer for MI355X (gfx950).  C ABI.
+ *
+ * The operation is the long-context decode indexer launch described on the
+ * sglang pull request page "sgl-project/sglang#48224" (the sgl-amd-mono #86
+ * commit body, Motivation): every cached key of each query row is scored and
+ * each row's exact top-2048 keys are selected.  The score of logical key s for
+ * row r is
+ *
+ *     score(r, s) = k_scale(s) * sum_{h<64} w[r][h] * max(q[r][h] . k(s), 0)
+ *
+ * with 64 index heads of 128 dims, q in bf16, k(s) the key's 128 E4M3 codes
+ * (decoded exactly) and k_scale(s) its fp32 scale (the same page, Modifications
+ * row 2: four 8-byte loads and the scale per 16-key group, i.e. 128 code bytes
+ * plus one scale per key).  Keys at or past a row's bound are neither scored
+ * nor selected (Modifications row 2: the store's mask drops them), so the
+ * bound is exclusive.
+ *
+ * Layouts (all row-major and contiguous unless a stride is given):
+ *   q           [rows][64][128]         bf16 (raw 16-bit patterns), 16-B aligned
+ *   w           [rows][64]              fp32, 16-B aligned
+ *   k_e4m3      [num_pages][64][128]    uint8 OCP E4M3FN codes, 16-B aligned
+ *   k_scale     [num_pages][64]         fp32
+ *   page_table  [pt_rows][pt_stride]    int32 physical page ids
+ *   row_pt      [rows]                  int32 page-table row of each query row
+ *   row_bound   [rows]                  int32 exclusive key bound, 0..max_bound
+ *   scores      [rows][score_stride]    fp32; entry s written only for s < bound
+ *   out_idx     [rows][topk]            int32 logical key indices
+ * Logical key s of row r lives in page page_table[row_pt[r]][s / 64], slot
+ * s % 64.  Only page-table entries below ceil(bound / 64) are read.
+ *
+ * Memory and ownership: every pointer argument except `p` is DEVICE memory
+ * owned by the caller.  The library allocates nothing, frees nothing and never
+ * synchronises; work is enqueued on `stream` (a hipStream_t; NULL = the
+ * default stream) and the call returns without waiting.  The workspace must
+ * be zero-filled once before first use (fp8idx_workspace_init does that on the
+ * stream); every launch leaves it zero-filled again, so it can be reused by
+ * later launches on the same stream, also for other problem shapes as long as
+ * rows <= 1024 (above that, re-initialise it when the row count grows).
+ * Concurrent launches must not share one workspace.
+ *
+ * Device arrays are trusted for sizes: row_bound[r] must be <= max_bound and
+ * row_pt[r] < pt_rows; values outside are clamped (bound) or make the row
+ * produce NaN scores (page-table row).  A page id outside [0, num_pages) is
+ * never dereferenced: the keys it covers score NaN.
+ *
+ * Errors: every call returns 0 on success or a negative FP8IDX_E* code.  All
+ * argument checks happen on the host before any device work is enqueued; an
+ * error return means nothing was enqueued (except FP8IDX_ELAUNCH, reported by
+ * the HIP runtime after an enqueue was attempted).  No exception crosses the
+ * ABI.
+ */
+#ifndef FP8IDX_H
+#define FP8IDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8IDX_ABI_VERSION 1
+#define FP8IDX_HEADS 64
+#define FP8IDX_HEAD_DIM 128
+#define FP8IDX_PAGE 64
+#define FP8IDX_MAX_TOPK 2048
+
+enum {
+    FP8IDX_OK = 0,
+    FP8IDX_EINVAL = -1,     /* invalid argument (null pointer, size, alignment) */
+    FP8IDX_EWORKSPACE = -2, /* workspace null or smaller than fp8idx_workspace_size */
+    FP8IDX_ELAUNCH = -3,    /* the HIP runtime reported an error for a launch */
+    FP8IDX_EDEVICE = -4     /* current device is not gfx950 / no device */
+};
+
+/* Problem descriptor (plain data, passed by host pointer).
+ *   rows         query rows (>= 1, <= 65535)
+ *   num_pages    pages in the key pool (>= 1)
+ *   pt_rows      rows of the page table (>= 1)
+ *   pt_stride    entries per page-table row (>= 1)
+ *   max_bound    upper bound of every row_bound (0 .. pt_stride*64)
+ *   topk         keys selected per row (1 .. 2048)
+ *   score_stride elements between score rows (>= max_bound when scores are
+ *                passed; ignored when they are not) */
+typedef struct fp8idx_problem {
+    int32_t rows;
+    int32_t num_pages;
+    int32_t pt_rows;
+    int32_t pt_stride;
+    int32_t max_bound;
+    int32_t topk;
+    int64_t score_stride;
+} fp8idx_problem_t;
+
+/* ABI version of the loaded library (FP8IDX_ABI_VERSION it was built with). */
+int fp8idx_abi_version(void);
+
+/* Static message for an error code (never NULL). */
+const char *fp8idx_strerror(int code);
+
+/* Bytes of device workspace for `p` (written to *bytes).  With
+ * scores_in_workspace != 0 the size includes room for the scores
+ * (indexer_launch with scores == NULL); with 0 it covers indexer_topk and
+ * indexer_launch with caller-provided scores.  The workspace pointer must be
+ * 256-byte aligned.  Host-only; touches no device. */
+int fp8idx_workspace_size(const fp8idx_problem_t *p, int scores_in_workspace, size_t *bytes);
+
+/* Zero-fills `ws_bytes` bytes (a multiple of 4) of workspace with a fill
+ * kernel on `stream`. */
+int fp8idx_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/* Scoring only: scores[r][s] for every s < row_bound[r] (the causal mask at
+ * the store); entries at or past the bound are left untouched.  Rows that
+ * share a page-table row and sit next to each other in the launch are scored
+ * together (each key is read from HBM once for the group).
+ * score_stride must be >= max_bound.  No workspace. */
+int indexer_score(const fp8idx_problem_t *p,
+                  const void *q_bf16, const float *w,
+                  const uint8_t *k_e4m3, const float *k_scale,
+                  const int32_t *page_table, const int32_t *row_pt,
+                  const int32_t *row_bound,
+                  float *scores, void *stream);
+
+/* Selection only: for each row, the exact top-topk of scores[r][0..bound)
+ * (descending value; equal values go to the lower key index; NaN ranks below
+ * every number; -0 equals +0).  out_idx[r] receives the selected logical
+ * indices in ascending index order; with fewer than topk keys all of them
+ * are returned and the remaining slots hold -1.  Uses p->rows, max_bound,
+ * topk and score_stride. */
+int indexer_topk(const fp8idx_problem_t *p,
+                 const float *scores, const int32_t *row_bound,
+                 int32_t *out_idx, void *ws, size_t ws_bytes, void *stream);
+
+/* The fused launch: scoring (with the selection's first radix digit counted
+ * in the scoring pass) followed by selection.  `scores` may be NULL (then the
+ * scores live in the workspace); when given, it receives exactly what
+ * indexer_score writes.  out_idx as for indexer_topk. */
+int indexer_launch(const fp8idx_problem_t *p,
+                   const void *q_bf16, const float *w,
+                   const uint8_t *k_e4m3, const float *k_scale,
+                   const int32_t *page_table, const int32_t *row_pt,
+                   const int32_t *row_bound,
+                   float *scores, int32_t *out_idx,
+                   void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8IDX_H */

@@ -39,7 +39,7 @@
 
 /* OCP 8-bit floating point, E4M3 ("FN": no infinities, S.1111.111 is NaN):
  * exponent bias 7; exponent field 0 is subnormal (m/8) * 2^-6. */
-double oracle_e4m3_decode(uint8_t b)
+static double e4m3_value(uint8_t b)
 {
     int s = (b >> 7) & 1;
     int e = (b >> 3) & 15;
@@ -55,7 +55,7 @@ double oracle_e4m3_decode(uint8_t b)
 }
 
 /* bfloat16: the upper 16 bits of an IEEE binary32. */
-double oracle_bf16_decode(uint16_t h)
+static double bf16_value(uint16_t h)
 {
     uint32_t u = (uint32_t)h << 16;
     float f;
@@ -63,9 +63,12 @@ double oracle_bf16_decode(uint16_t h)
     return (double)f;
 }
 
-/* One key-row: score and tolerance scale.  Returns 0, or -2 if the page
- * lookup is out of range. */
-static int score_one(const uint16_t *q_r, const float *w_r, const uint8_t *k8,
+double oracle_e4m3_decode(uint8_t b) { return e4m3_value(b); }
+double oracle_bf16_decode(uint16_t h) { return bf16_value(h); }
+
+/* One key-row: score and tolerance scale.  qd is the row's q decoded to
+ * fp64, [64][128].  Returns 0, or -2 if the page lookup is out of range. */
+static int score_one(const double *qd, const float *w_r, const uint8_t *k8,
                      const float *kscale, int num_pages, const int32_t *pt_row,
                      int64_t s, double *score, double *bnd)
 {
@@ -80,17 +83,24 @@ static int score_one(const uint16_t *q_r, const float *w_r, const uint8_t *k8,
     key = k8 + ((int64_t)page * ORC_PAGE + slot) * ORC_D;
     c = (double)kscale[(int64_t)page * ORC_PAGE + slot];
     for (i = 0; i < ORC_D; ++i)
-        kv[i] = oracle_e4m3_decode(key[i]);
+        kv[i] = e4m3_value(key[i]);
     for (h = 0; h < ORC_H; ++h) {
         double d = 0.0;
         for (i = 0; i < ORC_D; ++i)
-            d += oracle_bf16_decode(q_r[h * ORC_D + i]) * kv[i];
+            d += qd[h * ORC_D + i] * kv[i];
         acc += (double)w_r[h] * (d > 0.0 ? d : 0.0);
         accb += fabs((double)w_r[h]) * fabs(d);
     }
     *score = c * acc;
     *bnd = c * accb;
     return 0;
+}
+
+static void decode_q_row(const uint16_t *q_r, double *qd)
+{
+    int i;
+    for (i = 0; i < ORC_H * ORC_D; ++i)
+        qd[i] = bf16_value(q_r[i]);
 }
 
 /* Scores of row r for keys s in [s0, s1) (clipped to the row's bound).
@@ -104,6 +114,7 @@ int oracle_score_range(int r, int64_t s0, int64_t s1,
                        const int32_t *row_pt, const int32_t *row_bound,
                        double *out_score, double *out_bnd)
 {
+    double qd[ORC_H * ORC_D];
     int64_t s, b;
     int pr;
     if (!q || !w || !k8 || !kscale || !page_table || !row_pt || !row_bound || !out_score)
@@ -118,9 +129,10 @@ int oracle_score_range(int r, int64_t s0, int64_t s1,
         return -1;
     if (s1 > b)
         s1 = b;
+    decode_q_row(q + (int64_t)r * ORC_H * ORC_D, qd);
     for (s = s0; s < s1; ++s) {
         double sc, bd;
-        int rc = score_one(q + (int64_t)r * ORC_H * ORC_D, w + (int64_t)r * ORC_H, k8,
+        int rc = score_one(qd, w + (int64_t)r * ORC_H, k8,
                            kscale, num_pages, page_table + (int64_t)pr * pt_stride, s,
                            &sc, &bd);
         if (rc)
@@ -140,6 +152,7 @@ int oracle_score_samples(int64_t nsamp, const int32_t *samp_row, const int64_t *
                          const int32_t *row_pt, const int32_t *row_bound,
                          double *out_score, double *out_bnd)
 {
+    double qd[ORC_H * ORC_D];
     int64_t i;
     for (i = 0; i < nsamp; ++i) {
         int r = samp_row[i];
@@ -151,7 +164,8 @@ int oracle_score_samples(int64_t nsamp, const int32_t *samp_row, const int64_t *
             return -2;
         if (s < 0 || s >= row_bound[r] || s >= (int64_t)pt_stride * ORC_PAGE)
             return -1;
-        rc = score_one(q + (int64_t)r * ORC_H * ORC_D, w + (int64_t)r * ORC_H, k8, kscale,
+        decode_q_row(q + (int64_t)r * ORC_H * ORC_D, qd);
+        rc = score_one(qd, w + (int64_t)r * ORC_H, k8, kscale,
                        num_pages, page_table + (int64_t)pr * pt_stride, s, &sc, &bd);
         if (rc)
             return rc;

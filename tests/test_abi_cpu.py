@@ -1,0 +1,95 @@
+"""The C-ABI library loads, exports every function include/fp8idx.h declares,
+and rejects bad arguments on the host before touching any device (no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8idx.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import fp8_key_scoring_amd as fk
+    if not os.path.exists(fk.LIB_PATH):
+        from fp8_key_scoring_amd import build
+        build.build()
+    return fk.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("indexer_score", "indexer_topk", "indexer_launch", "fp8idx_workspace_size",
+              "fp8idx_workspace_init", "fp8idx_abi_version", "fp8idx_strerror"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_strerror(lib):
+    import fp8_key_scoring_amd as fk
+    assert fk.abi_version() == 1
+    for code in (0, -1, -2, -3, -4, 7):
+        assert lib.fp8idx_strerror(code)
+
+
+def test_problem_struct_layout():
+    import fp8_key_scoring_amd as fk
+    assert ctypes.sizeof(fk.Problem) == 32
+    assert fk.Problem.score_stride.offset == 24
+
+
+def test_workspace_size(lib):
+    import fp8_key_scoring_amd as fk
+    p = fk.make_problem(rows=4, num_pages=8192, pt_rows=1, pt_stride=8192, max_bound=524288)
+    a = fk.workspace_size(p, False)
+    b = fk.workspace_size(p, True)
+    assert 0 < a < b and b - a >= 4 * 524288 * 4
+    with pytest.raises(fk.Fp8IdxError):
+        fk.workspace_size(fk.make_problem(0, 1, 1, 1, 0), False)
+
+
+def _call_score(lib, prob, ptrs):
+    import fp8_key_scoring_amd as fk
+    return lib.indexer_score(ctypes.byref(prob), *ptrs, None)
+
+
+def test_host_side_argument_errors(lib):
+    import fp8_key_scoring_amd as fk
+    good = [0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000, 0x8000]   # never dereferenced
+    base = dict(rows=4, num_pages=16, pt_rows=1, pt_stride=16, max_bound=1024, topk=2048,
+                score_stride=1024)
+    bad = [dict(rows=0), dict(rows=70000), dict(topk=0), dict(topk=2049), dict(max_bound=-1),
+           dict(max_bound=16 * 64 + 1), dict(num_pages=0), dict(pt_stride=0), dict(score_stride=1000)]
+    for b in bad:
+        p = fk.make_problem(**{**base, **b})
+        assert _call_score(lib, p, good) == -1, b
+    p = fk.make_problem(**base)
+    for i in range(len(good)):
+        ptrs = list(good)
+        ptrs[i] = None
+        assert _call_score(lib, p, ptrs) == -1
+    misaligned = list(good)
+    misaligned[0] = 0x1008   # q must be 16-byte aligned
+    assert _call_score(lib, p, misaligned) == -1
+    # workspace too small / missing
+    rc = lib.indexer_topk(ctypes.byref(p), 0x1000, 0x2000, 0x3000, None, 0, None)
+    assert rc == -2
+    rc = lib.indexer_topk(ctypes.byref(p), 0x1000, 0x2000, 0x3000, 0x100000, 16, None)
+    assert rc == -2
+    rc = lib.indexer_launch(ctypes.byref(p), *good[:7], None, None, 0x100000, 1 << 30, None)
+    assert rc == -1   # out_idx missing
+    assert lib.fp8idx_workspace_init(None, 256, None) == -1
+    assert lib.fp8idx_workspace_init(0x100001, 256, None) == -1

@@ -1,0 +1,107 @@
+"""Bitwise invariants of the HIP path on MI355X: determinism, the fused launch
+against the separate calls, scores kept in the workspace, physical page
+relabelling, row-set independence, workspace reuse and out-of-range page ids."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_key_scoring_amd as fk
+import synthetic as syn
+from gpu_util import check_topk_exact, run_launch, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _prob(seed=21, n=40000):
+    return syn.build_problem("inv", seed, [n, n // 2], syn.verify_rows(0, n) + syn.verify_rows(1, n // 2),
+                             dup_frac=0.01)
+
+
+def test_two_launches_are_bitwise_equal():
+    p = _prob()
+    say("[gpu] determinism")
+    s1, o1 = run_launch(p)
+    s2, o2 = run_launch(p)
+    assert np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+    assert np.array_equal(o1, o2)
+
+
+def test_launch_equals_score_then_topk():
+    p = _prob(22)
+    say("[gpu] launch vs score + topk")
+    s1, o1 = run_launch(p)
+    d = to_device(p)
+    sc = torch.full((p.rows, p.max_bound), float("nan"), dtype=torch.float32, device="cuda:0")
+    fk.indexer_score(**d, max_bound=p.max_bound, scores=sc)
+    o2 = fk.indexer_topk(sc, d["row_bound"], max_bound=p.max_bound, topk=p.topk)
+    torch.cuda.synchronize()
+    assert np.array_equal(s1.view(np.uint32), sc.cpu().numpy().view(np.uint32))
+    assert np.array_equal(o1, o2.cpu().numpy())
+
+
+def test_scores_in_workspace():
+    p = _prob(23)
+    say("[gpu] scores kept in the workspace")
+    _, o1 = run_launch(p)
+    _, o2 = run_launch(p, keep_scores=False)
+    assert np.array_equal(o1, o2)
+
+
+def test_page_relabel_invariance():
+    p = _prob(24)
+    say("[gpu] page relabel")
+    s1, o1 = run_launch(p)
+    relabel = np.random.default_rng(5).permutation(p.num_pages)
+    k8 = np.empty_like(p.k_e4m3)
+    ks = np.empty_like(p.k_scale)
+    k8[relabel] = p.k_e4m3
+    ks[relabel] = p.k_scale
+    pt = np.where(p.page_table >= 0, relabel[np.maximum(p.page_table, 0)], -1).astype(np.int32)
+    p2 = syn.Problem(**{**p.__dict__, "k_e4m3": k8, "k_scale": ks, "page_table": pt})
+    s2, o2 = run_launch(p2)
+    assert np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+    assert np.array_equal(o1, o2)
+
+
+def test_rows_scored_alone_match_rows_scored_together():
+    p = _prob(25)
+    say("[gpu] row-set independence")
+    s_all, o_all = run_launch(p)
+    for r in (0, 2, 5):
+        sub = syn.Problem(**{**p.__dict__, "q_bf16": p.q_bf16[r:r + 1].copy(), "w": p.w[r:r + 1].copy(),
+                             "row_pt": p.row_pt[r:r + 1].copy(), "row_bound": p.row_bound[r:r + 1].copy()})
+        s1, o1 = run_launch(sub)
+        b = int(p.row_bound[r])
+        assert np.array_equal(s1[0, :b].view(np.uint32), s_all[r, :b].view(np.uint32))
+        assert np.array_equal(o1[0], o_all[r])
+
+
+def test_workspace_reuse_across_problems():
+    say("[gpu] workspace reuse")
+    big = _prob(26, n=60000)
+    small = syn.build_problem("small", 27, [5000], syn.verify_rows(0, 5000))
+    prob = fk.make_problem(rows=8, num_pages=big.num_pages, pt_rows=2, pt_stride=big.pt_stride,
+                           max_bound=big.max_bound, topk=2048)
+    ws = fk.new_workspace(prob, True, "cuda:0")
+    ref_big = run_launch(big)[1]
+    ref_small = run_launch(small)[1]
+    for p, ref in [(big, ref_big), (small, ref_small), (big, ref_big), (small, ref_small), (big, ref_big)]:
+        _, o = run_launch(p, keep_scores=False, workspace=ws)
+        assert np.array_equal(o, ref)
+
+
+def test_out_of_range_page_ids_score_nan():
+    p = syn.build_problem("badpage", 28, [4096], syn.verify_rows(0, 4096))
+    p.page_table[0, 3] = p.num_pages + 100     # keys 192..255
+    p.page_table[0, 10] = -7                   # keys 640..703
+    say("[gpu] out-of-range page ids")
+    scores, out = run_launch(p)
+    bad = np.zeros(4096, bool)
+    bad[192:256] = True
+    bad[640:704] = True
+    for r in range(p.rows):
+        b = int(p.row_bound[r])
+        assert np.all(np.isnan(scores[r, :b][bad[:b]]))
+        assert np.all(np.isfinite(scores[r, :b][~bad[:b]]))
+    check_topk_exact(p, scores, out)
+    assert not np.any(bad[out[out >= 0]])

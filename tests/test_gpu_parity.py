@@ -1,0 +1,126 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on MI355X.
+
+Acceptance per row:
+  * scores: |gpu - ref| <= 1e-3 * B + 1e-6, B = scale * sum_h |w_h| |q_h . k|;
+  * selection: the set equals the oracle's exact top-k of the GPU's own scores
+    (ties to the lower index), in ascending index order, -1 padded;
+  * overlap with the oracle's top-k of its own fp64 scores >= 99.9%;
+  * entries at or past a row's bound are never written.
+"""
+import numpy as np
+import pytest
+
+import synthetic as syn
+from gpu_util import (OVERLAP_MIN, check_scores_full, check_scores_sampled, check_topk_exact,
+                      check_untouched_past_bound, oracle_rows, overlap, run_launch, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def full_check(p, label):
+    say(f"[gpu] {label}: rows={p.rows} max_bound={p.max_bound} topk={p.topk}")
+    scores, out = run_launch(p)
+    check_untouched_past_bound(p, scores)
+    ref = oracle_rows(p, range(p.rows))
+    worst = check_scores_full(p, scores, ref)
+    check_topk_exact(p, scores, out)
+    ov = overlap(p, ref, out)
+    say(f"[gpu] {label}: worst err/tol {worst:.3g}, worst overlap {ov:.5f}")
+    assert ov >= OVERLAP_MIN
+    return scores, out
+
+
+def test_c1_one_row_8k():
+    full_check(syn.make_config(1), "c1")
+
+
+def test_c2_four_rows_128k():
+    full_check(syn.make_config(2), "c2")
+
+
+SMALL = [
+    ("r1_ragged", [5000], [(0, 5000)]),
+    ("r4_ragged", [8983], syn.verify_rows(0, 8983)),
+    ("r2", [7777], [(0, 7777), (0, 7770)]),
+    ("r3", [6000], [(0, 6000), (0, 5999), (0, 5998)]),
+    ("r5_same_request", [10000], [(0, 10000 - j) for j in range(5)]),
+    ("interleaved_requests", [6000, 7000], [(0, 6000), (1, 7000), (0, 5999), (1, 6999)]),
+    ("unaligned_groups", [3000, 9000], [(0, 3000), (0, 2999), (1, 9000), (1, 8999), (1, 8998), (1, 8997)]),
+    ("many_requests", [2500 + 977 * i for i in range(10)],
+     [rw for i in range(10) for rw in syn.verify_rows(i, 2500 + 977 * i)]),
+]
+
+
+@pytest.mark.parametrize("name,lens,rows", SMALL, ids=[s[0] for s in SMALL])
+def test_small_shapes(name, lens, rows):
+    full_check(syn.build_problem(name, 77, lens, rows), name)
+
+
+def test_edge_bounds():
+    bounds = [0, 1, 63, 64, 65, 2047, 2048, 2049, 3000]
+    p = syn.build_problem("edge_bounds", 5, [3000], [(0, b) for b in bounds])
+    scores, out = full_check(p, "edge_bounds")
+    assert np.all(out[0] == -1)
+    assert out[1].tolist()[:2] == [0, -1]
+    assert out[4].tolist()[:65] == list(range(65)) and np.all(out[4][65:] == -1)
+    assert out[6].tolist() == list(range(2048))
+
+
+@pytest.mark.parametrize("k", [1, 100, 2047])
+def test_smaller_topk(k):
+    p = syn.build_problem(f"topk{k}", 9, [20000], syn.verify_rows(0, 20000), topk=k)
+    full_check(p, f"topk{k}")
+
+
+def test_all_equal_keys_take_the_lowest_indices():
+    # every score of a row is equal: the exact answer is keys 0..k-1, reached
+    # through the heavy-tie path (the prefix bin holds more than the candidate cap)
+    p = syn.build_problem("all_equal", 3, [20000], [(0, 20000), (0, 19000)], key_mode="all_equal")
+    scores, out = full_check(p, "all_equal")
+    for r in range(p.rows):
+        assert np.unique(scores[r, :p.row_bound[r]]).size == 1
+        assert out[r].tolist() == list(range(2048))
+
+
+def test_ties_straddling_the_threshold():
+    p = syn.scale_tie_problem(n=12000)
+    scores, out = full_check(p, "scale_ties")
+    vals = np.unique(scores[0, :12000])
+    assert vals.size == 3
+    s = scores[0, :12000]
+    top = np.nonzero(s == vals[2])[0]
+    mid = np.nonzero(s == vals[1])[0]
+    expect = np.sort(np.concatenate([top, mid[:2048 - top.size]]))
+    assert np.array_equal(out[0], expect)
+
+
+def test_extreme_codes():
+    p = syn.build_problem("extreme", 4, [9000], syn.verify_rows(0, 9000), key_mode="extreme")
+    full_check(p, "extreme")
+
+
+def _big(idx, overlap_rows=None):
+    p = syn.make_config(idx)
+    say(f"[gpu] {p.name}: rows={p.rows} max_bound={p.max_bound}")
+    scores, out = run_launch(p)
+    check_untouched_past_bound(p, scores)
+    w = check_scores_sampled(p, scores)
+    check_topk_exact(p, scores, out)
+    rows = range(p.rows) if overlap_rows is None else overlap_rows
+    ref = oracle_rows(p, rows)
+    check_scores_full(p, scores, ref, rows)
+    ov = overlap(p, ref, out, rows)
+    say(f"[gpu] {p.name}: sampled worst err/tol {w:.3g}, worst overlap {ov:.5f}")
+    assert ov >= OVERLAP_MIN
+
+
+def test_c3_four_rows_512k():
+    _big(3)
+
+
+def test_c4_two_requests_8_rows():
+    _big(4)
+
+
+def test_c5_batch_256_rows():
+    _big(5, overlap_rows=[0, 1, 2, 3, 100, 101, 254, 255])
