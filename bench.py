@@ -1,0 +1,215 @@
+"""Benchmark of the fused indexer launch (scoring + exact top-2048) on one MI355X.
+
+Workload: one request's 4 verify rows over 524,288 paged E4M3 keys (bounds
+n-3..n), 64 heads x 128, page 64, top-2048.  A step is one indexer_launch
+call.  Inputs sit in HBM before timing starts; the timed steps rotate over
+several copies of the key pool and page table (together larger than the
+256 MB MALL) so each step streams its keys from HBM.
+
+Prints one JSON line.  Extra keys: "roofline" for the scoring kernel (timed
+per launch with HIP events on the launch stream) and "cpu_baseline" (the CPU
+oracle on a bounded sample of the same workload, on the host's cores).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "indexer keys scored/s and µs/launch at 512K keys, 4 rows; % of roofline"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+FLOP_PER_KEY_ROW = 2 * 64 * 128
+BYTES_PER_KEY = 128 + 4       # E4M3 codes + fp32 scale
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--pools", type=int, default=4, help="key-pool copies rotated over")
+    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (3 = 512K keys x 4 rows)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a plain device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(p):
+    """Bytes one launch must move at least: each distinct key once (codes +
+    scale), the page-table entries, q/w/bounds per row, the selected indices."""
+    distinct = p.distinct_keys()
+    pages = sum(-(-int(b) // 64) for b in _group_max(p).values())
+    per_row = 64 * 128 * 2 + 64 * 4 + 8
+    out = 4 * sum(min(p.topk, int(b)) for b in p.row_bound)
+    return BYTES_PER_KEY * distinct + 4 * pages + per_row * p.rows + out
+
+
+def _group_max(p):
+    g = {}
+    for r in range(p.rows):
+        k = int(p.row_pt[r])
+        g[k] = max(g.get(k, 0), int(p.row_bound[r]))
+    return g
+
+
+def cpu_baseline(p, seconds):
+    """The oracle (scores + exact top-k) on a bounded sample of the workload,
+    sharded over host threads.  Returns the metric-unit rate."""
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+    oracle.build(force=False)
+    threads = max(1, min(16, os.cpu_count() or 1))
+    # calibrate: one thread, 2048 keys of row 0
+    t0 = time.perf_counter()
+    oracle.score_range(p, 0, 0, 2048)
+    per_key = (time.perf_counter() - t0) / 2048
+    keys_per_row = int(min(p.row_bound.min(), max(4096, seconds / per_key / p.rows)))
+    keys_per_row -= keys_per_row % 1024
+    tasks = [(r, s0, min(keys_per_row, s0 + 4096)) for r in range(p.rows) for s0 in range(0, keys_per_row, 4096)]
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(lambda t: oracle.score_range(p, *t)[0], tasks))
+    rows = {}
+    for (r, s0, s1), sc in zip(tasks, parts):
+        rows.setdefault(r, []).append(sc)
+    for r in rows:
+        oracle.topk(np.concatenate(rows[r]), p.topk)
+    wall = time.perf_counter() - t0
+    n = keys_per_row * p.rows
+    return {"value": n / wall, "unit": "keys/s", "cores": threads, "kind": "oracle",
+            "sample": f"{p.rows} rows x first {keys_per_row} keys of the same workload: fp64 scores "
+                      f"+ exact top-{p.topk} of the sample, {threads} host threads, {wall:.2f} s"}
+
+
+def copy_calib():
+    import torch
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calib_bytes_read_per_copy": n, "copies": 5}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build times the single-GPU indexer launch "
+              "(use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calib:
+        copy_calib()
+        return
+    import torch
+    import fp8_key_scoring_amd as fk
+    import synthetic as syn
+
+    fk.load_library()
+    dev = "cuda:0"
+    p = syn.make_config(args.config)
+    d = syn.device_arrays(p, dev)
+    pools = [d]
+    for i in range(1, args.pools):
+        pools.append({**d, "k_e4m3": d["k_e4m3"].clone(), "k_scale": d["k_scale"].clone(),
+                      "page_table": d["page_table"].clone()})
+    mb = p.max_bound
+    prob = fk._problem_from(d["q"], d["k_e4m3"], d["page_table"], mb, p.topk, 0)
+    ws = fk.new_workspace(prob, True, dev)
+    outs = torch.empty((p.rows, p.topk), dtype=torch.int32, device=dev)
+    scores = torch.empty((p.rows, mb), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        fk.indexer_launch(**pools[i % len(pools)], max_bound=mb, topk=p.topk, out_idx=outs, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+
+    # hot variant: one pool (keys may stay in the MALL between launches)
+    for i in range(args.warmup):
+        fk.indexer_launch(**d, max_bound=mb, topk=p.topk, out_idx=outs, workspace=ws)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        fk.indexer_launch(**d, max_bound=mb, topk=p.topk, out_idx=outs, workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step_hot = e0.elapsed_time(e1) / args.steps
+
+    # scoring kernel alone, one event pair per launch on the launch stream
+    n_k = max(20, min(args.steps, 200))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_k)]
+    for i in range(args.warmup):
+        fk.indexer_score(**pools[i % len(pools)], max_bound=mb, scores=scores)
+    torch.cuda.synchronize()
+    for i in range(n_k):
+        ev[i][0].record(stream)
+        fk.indexer_score(**pools[i % len(pools)], max_bound=mb, scores=scores)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    score_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    key_rows = p.key_rows()
+    flops = FLOP_PER_KEY_ROW * key_rows
+    abytes = algorithmic_bytes(p)
+    ach_tflops = flops / (score_ms * 1e-3) / 1e12
+    ach_gbs = abytes / (score_ms * 1e-3) / 1e9
+    mfma_bound = flops / (PEAK_BF16_TFLOPS * 1e12) >= abytes / (PEAK_HBM_GBS * 1e9)
+    roof = ({"bound": "mfma", "achieved": round(ach_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+             "unit": "TFLOP/s", "frac": round(ach_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None}
+            if mfma_bound else
+            {"bound": "hbm", "achieved": round(ach_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": round(ach_gbs / PEAK_HBM_GBS, 4), "traffic": None})
+    roof.update({"kernel": "score_kernel (indexer_score)", "kernel_us": round(score_ms * 1e3, 2),
+                 "algorithmic_flops": flops, "algorithmic_bytes": abytes,
+                 "hbm_gbs_at_kernel_time": round(ach_gbs, 1)})
+    step_roof_s = max(flops / (PEAK_BF16_TFLOPS * 1e12), abytes / (PEAK_HBM_GBS * 1e9))
+
+    res = {
+        "metric": METRIC,
+        "value": key_rows / (ms_step * 1e-3),
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "us_per_launch": ms_step * 1e3,
+        "us_per_launch_hot": ms_step_hot * 1e3,
+        "launch_roofline_frac": round(step_roof_s / (ms_step * 1e-3), 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": p.name, "rows": p.rows, "keys": int(p.max_bound), "key_rows": key_rows,
+                   "heads": 64, "head_dim": 128, "page": 64, "topk": p.topk, "kv": "e4m3",
+                   "pools_rotated": len(pools)},
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

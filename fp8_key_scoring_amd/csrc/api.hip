@@ -103,7 +103,8 @@ int run_select(const fp8idx_problem_t *p, const float *scores, int64_t sstride,
     hipError_t e = hipSuccess;
     if (need_hist1 && (e = launch_hist1(a, st)) != hipSuccess) return to_code(e);
     if ((e = launch_refine(a, st)) != hipSuccess) return to_code(e);
-    return to_code(launch_gather(a, st));
+    if ((e = launch_gather(a, st)) != hipSuccess) return to_code(e);
+    return to_code(launch_finalize(a, st));
 }
 
 }  // namespace

@@ -21,9 +21,10 @@ constexpr int kKeysPerMfma = 16;   // one 16x16x32 MFMA column block = 16 keys
 
 // Selection.
 constexpr int kSelThreads = 256;
-constexpr int kSelChunkMin = 8192;  // keys per selection workgroup (at least)
-constexpr int kSelMaxWgs = 64;      // selection workgroups per row (at most)
-constexpr int kCandCap = 4096;      // candidates kept per row for the final sort
+constexpr int kSelUnroll = 32;                      // scores in flight per thread
+constexpr int kSelTile = kSelThreads * kSelUnroll;  // keys per workgroup step
+constexpr int kSelMaxWgs = 64;                      // selection workgroups per row (at most)
+constexpr int kCandCap = 4096;                      // candidates kept per row for the final sort
 constexpr int kZeroRows = 1024;    // rows the zero block is laid out for (at least)
 constexpr int kDigit1Bits = 6;      // first radix digit (counted while scoring)
 constexpr int kDigit2Bits = 8;      // second radix digit
@@ -32,7 +33,7 @@ constexpr int kDigit2Shift = kDigit1Shift - kDigit2Bits;     // 18
 constexpr int kBins1 = 1 << kDigit1Bits;                     // 64
 constexpr int kBins2 = 1 << kDigit2Bits;                     // 256
 
-// Per-row selection state, written by the last refine workgroup of a row.
+// Per-row selection state, written by the first gather workgroup of a row.
 struct RowState {
     uint32_t b1;      // first-digit bin holding the k-th largest key
     uint32_t b2;      // second-digit bin inside b1 holding it
@@ -42,19 +43,19 @@ struct RowState {
     uint32_t pad[3];
 };
 
-// Workspace layout.  Counters and histograms must be zero before a launch;
-// every launch leaves them zero again.  They sit in one block at the start,
-// laid out for max(rows, kZeroRows) rows, so the block has the same offsets
-// for every problem of up to kZeroRows rows and a workspace can be reused
-// across problem shapes; the rest of the workspace is scratch.
+// Workspace layout.  The histograms and the candidate counters must be zero
+// before a launch; every launch leaves them zero again.  They sit in one block
+// at the start, laid out for max(rows, kZeroRows) rows, so the block has the
+// same offsets for every problem of up to kZeroRows rows and a workspace can
+// be reused across problem shapes; the rest of the workspace is scratch that
+// each launch writes before it reads.
 struct WsLayout {
-    size_t hist1;      // u32 [rows][64]
-    size_t cnt2;       // u32 [rows]   refine completion counters
-    size_t cnt3;       // u32 [rows]   gather completion counters
-    size_t sure_slot;  // u32 [rows]
-    size_t cand_slot;  // u32 [rows]
+    size_t hist1;      // u32 [rz][64]      first-digit counts
+    size_t hist2;      // u32 [rz][256]     second-digit counts inside the first-digit bin
+    size_t cand_slot;  // u32 [rz]          candidate slots taken
     size_t state;      // RowState [rows]
-    size_t hist2p;     // u32 [rows][sel_wgs][256]   per-workgroup partials
+    size_t sure_cnt;   // u32 [rows][sel_wgs]             sure keys per gather workgroup
+    size_t sure_list;  // i32 [rows][sel_wgs][kMaxTopk]   their indices, ascending
     size_t cand;       // u64 [rows][kCandCap]
     size_t scores;     // f32 [rows][sstride]  (only when the caller gives none)
     size_t total;
@@ -67,24 +68,23 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 inline WsLayout ws_layout(int rows, int max_bound, bool own_scores) {
     WsLayout L{};
-    int64_t mb = max_bound > 0 ? max_bound : 1;
-    int s = (int)((mb + kSelChunkMin - 1) / kSelChunkMin);
-    if (s < 1) s = 1;
-    if (s > kSelMaxWgs) s = kSelMaxWgs;
-    L.sel_wgs = s;
-    int64_t ch = (mb + s - 1) / s;
-    L.sel_chunk = (ch + kSelThreads - 1) / kSelThreads * kSelThreads;
+    const int64_t mb = max_bound > 0 ? max_bound : 1;
+    int n = (int)((mb + kSelTile - 1) / kSelTile);
+    if (n < 1) n = 1;
+    if (n > kSelMaxWgs) n = kSelMaxWgs;
+    const int64_t ch = (mb + n - 1) / n;
+    L.sel_wgs = n;
+    L.sel_chunk = (ch + kSelTile - 1) / kSelTile * kSelTile;   // whole scan tiles
     L.sstride = (int64_t)align_up((size_t)mb, 64);
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
     const size_t rz = (size_t)(rows > kZeroRows ? rows : kZeroRows);
     L.hist1 = take(rz * kBins1 * 4);
-    L.cnt2 = take(rz * 4);
-    L.cnt3 = take(rz * 4);
-    L.sure_slot = take(rz * 4);
+    L.hist2 = take(rz * kBins2 * 4);
     L.cand_slot = take(rz * 4);
     L.state = take((size_t)rows * sizeof(RowState));
-    L.hist2p = take((size_t)rows * s * kBins2 * 4);
+    L.sure_cnt = take((size_t)rows * n * 4);
+    L.sure_list = take((size_t)rows * n * kMaxTopk * 4);
     L.cand = take((size_t)rows * kCandCap * 8);
     L.scores = own_scores ? take((size_t)rows * (size_t)L.sstride * 4) : off;
     L.total = off;
@@ -128,6 +128,7 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t st);
 hipError_t launch_hist1(const SelectArgs &a, hipStream_t st);
 hipError_t launch_refine(const SelectArgs &a, hipStream_t st);
 hipError_t launch_gather(const SelectArgs &a, hipStream_t st);
+hipError_t launch_finalize(const SelectArgs &a, hipStream_t st);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
 
 }  // namespace fp8idx
