@@ -20,18 +20,23 @@ constexpr int kGroupRows = 4;
 constexpr int kKeysPerMfma = 16;   // one 16x16x32 MFMA column block = 16 keys
 
 // Selection.
-constexpr int kSelThreads = 256;
-constexpr int kSelUnroll = 32;                      // scores in flight per thread
+constexpr int kSelThreads = 1024;                   // 16 waves: 4 per SIMD hide LDS latency
+constexpr int kSelUnroll = 8;                       // scores in flight per thread
 constexpr int kSelTile = kSelThreads * kSelUnroll;  // keys per workgroup step
 constexpr int kSelMaxWgs = 64;                      // selection workgroups per row (at most)
-constexpr int kCandCap = 4096;                      // candidates kept per row for the final sort
+constexpr int kCandSlice = 1024;                    // candidates one gather workgroup keeps
+constexpr int kCandCap = 4096;                      // candidates one row may have (else fallback)
+constexpr int kTieCap = 1024;                       // keys in the third-digit bin finalize ranks
 constexpr int kZeroRows = 1024;    // rows the zero block is laid out for (at least)
 constexpr int kDigit1Bits = 6;      // first radix digit (counted while scoring)
 constexpr int kDigit2Bits = 8;      // second radix digit
 constexpr int kDigit1Shift = 32 - kDigit1Bits;               // 26
 constexpr int kDigit2Shift = kDigit1Shift - kDigit2Bits;     // 18
+constexpr int kDigit3Bits = 8;      // third radix digit (counted over the candidates)
+constexpr int kDigit3Shift = kDigit2Shift - kDigit3Bits;     // 10
 constexpr int kBins1 = 1 << kDigit1Bits;                     // 64
 constexpr int kBins2 = 1 << kDigit2Bits;                     // 256
+constexpr int kBins3 = 1 << kDigit3Bits;                     // 256
 
 // Per-row selection state, written by the first gather workgroup of a row.
 struct RowState {
@@ -43,20 +48,21 @@ struct RowState {
     uint32_t pad[3];
 };
 
-// Workspace layout.  The histograms and the candidate counters must be zero
-// before a launch; every launch leaves them zero again.  They sit in one block
-// at the start, laid out for max(rows, kZeroRows) rows, so the block has the
-// same offsets for every problem of up to kZeroRows rows and a workspace can
-// be reused across problem shapes; the rest of the workspace is scratch that
-// each launch writes before it reads.
+// Workspace layout.  The histograms must be zero before a launch; every
+// launch leaves them zero again.  They sit in one block at the start, laid out
+// for max(rows, kZeroRows) rows, so the block has the same offsets for every
+// problem of up to kZeroRows rows and a workspace can be reused across problem
+// shapes; the rest of the workspace is scratch that each launch writes before
+// it reads.
 struct WsLayout {
     size_t hist1;      // u32 [rz][64]      first-digit counts
     size_t hist2;      // u32 [rz][256]     second-digit counts inside the first-digit bin
-    size_t cand_slot;  // u32 [rz]          candidate slots taken
+    size_t hist3;      // u32 [rz][256]     third-digit counts of the candidates
     size_t state;      // RowState [rows]
-    size_t sure_cnt;   // u32 [rows][sel_wgs]             sure keys per gather workgroup
-    size_t sure_list;  // i32 [rows][sel_wgs][kMaxTopk]   their indices, ascending
-    size_t cand;       // u64 [rows][kCandCap]
+    size_t sure_cnt;   // u32 [rows][sel_wgs]              sure keys per gather workgroup
+    size_t cand_cnt;   // u32 [rows][sel_wgs]              candidates per gather workgroup
+    size_t sure_list;  // i32 [rows][sel_wgs][kMaxTopk]    their indices, ascending
+    size_t cand_list;  // u64 [rows][sel_wgs][kCandSlice]  key << 32 | index, ascending index
     size_t scores;     // f32 [rows][sstride]  (only when the caller gives none)
     size_t total;
     int sel_wgs;
@@ -74,18 +80,19 @@ inline WsLayout ws_layout(int rows, int max_bound, bool own_scores) {
     if (n > kSelMaxWgs) n = kSelMaxWgs;
     const int64_t ch = (mb + n - 1) / n;
     L.sel_wgs = n;
-    L.sel_chunk = (ch + kSelTile - 1) / kSelTile * kSelTile;   // whole scan tiles
+    L.sel_chunk = (ch + kSelTile - 1) / kSelTile * kSelTile;   // whole scan steps
     L.sstride = (int64_t)align_up((size_t)mb, 64);
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
     const size_t rz = (size_t)(rows > kZeroRows ? rows : kZeroRows);
     L.hist1 = take(rz * kBins1 * 4);
     L.hist2 = take(rz * kBins2 * 4);
-    L.cand_slot = take(rz * 4);
+    L.hist3 = take(rz * kBins3 * 4);
     L.state = take((size_t)rows * sizeof(RowState));
     L.sure_cnt = take((size_t)rows * n * 4);
+    L.cand_cnt = take((size_t)rows * n * 4);
     L.sure_list = take((size_t)rows * n * kMaxTopk * 4);
-    L.cand = take((size_t)rows * kCandCap * 8);
+    L.cand_list = take((size_t)rows * n * kCandSlice * 8);
     L.scores = own_scores ? take((size_t)rows * (size_t)L.sstride * 4) : off;
     L.total = off;
     return L;

@@ -10,6 +10,7 @@
 // Radix key: the order-preserving fp32 -> u32 map (common.h).  Digits:
 //   d1 = bits 31..26 (64 bins)   counted by the scoring pass, or by hist1_kernel
 //   d2 = bits 25..18 (256 bins)  counted by refine_kernel inside the d1 bin
+//   d3 = bits 17..10 (256 bins)  counted by gather_kernel over the candidates
 // The 14-bit prefix (d1, d2) of the k-th largest key splits a row into
 //   "sure" keys (prefix above it: all selected) and
 //   candidates (prefix equal: the remaining `need` are chosen among them).
@@ -20,24 +21,29 @@
 //   refine   second-digit counts inside the first-digit bin, added to the
 //            row's histogram with one atomic per non-empty bin per workgroup;
 //   gather   every workgroup derives the same split from the two histograms,
-//            writes its sure keys in index order to its own slice of the
-//            workspace (ballot prefix sums, no atomics) and appends its
-//            candidates to the row's list (one slot reservation);
-//   finalize one workgroup per row sorts the candidates by (key desc, index
-//            asc), takes `need`, and merges them with the concatenated sure
-//            slices by binary search, so the row's output comes out in
-//            ascending index order (deterministic bytes) without a full sort.
-// Each scan step keeps 32 loads in flight per thread (8192 keys per
-// workgroup), so a workgroup's pass over its chunk is one memory round trip.
-// If a row has more than kCandCap candidates (heavy ties) finalize resolves
-// the remaining 18 bits itself with three more digit passes over the row and
-// takes exact ties in index order.
+//            writes its sure keys and its candidates, each in index order, to
+//            its own slices of the workspace (ballot prefix sums, no
+//            atomics), and adds its candidates' third digits to the row's
+//            third histogram;
+//   finalize one workgroup per row: the third digit's bin of the k-th key
+//            splits the candidates once more; all above it are taken, the few
+//            inside it are ranked by (key desc, index asc); a stable
+//            compaction keeps index order, and a merge by binary search with
+//            the concatenated sure slices writes the row's output in
+//            ascending index order (deterministic bytes) with no sort.
+// Workgroups are 1024 threads (four waves per SIMD hide LDS latency) and each
+// thread keeps 8 score loads in flight, so a workgroup's scan of its 8192
+// keys is one memory round trip.  Rows whose candidates overflow the slices
+// (heavy ties) are resolved exactly by finalize rescanning the row with three
+// more digit passes and taking ties in index order.
 #include "common.h"
 
 namespace fp8idx {
 
-static_assert(kSelThreads == kBins2, "one thread per second-digit bin");
-static_assert(kSelThreads / 64 * kSelUnroll == 128, "gather prefix: two entries per lane");
+constexpr int kWaves = kSelThreads / 64;
+static_assert(kSelThreads == 1024, "finalize keeps four candidates per thread");
+static_assert(kSelUnroll * kWaves == 128, "gather prefix: two entries per lane");
+static_assert(kCandCap == 4 * kSelThreads, "finalize keeps four candidates per thread");
 
 __device__ __forceinline__ uint32_t lane_prefix(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -68,10 +74,51 @@ __device__ void wave_find_bin(const uint32_t *h, int per, uint32_t need, int lan
     }
 }
 
-// One scan step: thread t gets the radix keys of keys base + j*256 + t for
-// j < kSelUnroll; all loads are issued before any is used.  Keys at or past
-// s1 are not read (their slot gets key 0; callers test s < s1).
-__device__ __forceinline__ void load_tile(const float *row, int64_t base, int64_t s1,
+// Executed by one full wave: c[0..128) becomes its exclusive prefix sum (in
+// index order); *total gets the sum.
+__device__ void wave_scan128(uint32_t *c, uint32_t *total, int lane) {
+    const uint32_t c0 = c[2 * lane], c1 = c[2 * lane + 1];
+    uint32_t incl = c0 + c1;
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+    }
+    const uint32_t excl = incl - c0 - c1;
+    c[2 * lane] = excl;
+    c[2 * lane + 1] = excl + c0;
+    if (lane == 63) *total = incl;
+}
+
+// Exclusive prefix sum of v over the workgroup in thread order (*total: the sum).
+__device__ uint32_t block_scan(uint32_t v, uint32_t *wsum, uint32_t *total) {
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    uint32_t incl = v;
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    if (t < 64) {
+        const uint32_t w = lane < kWaves ? wsum[lane] : 0u;
+        uint32_t wi = w;
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_up(wi, off);
+            if (lane >= off) wi += y;
+        }
+        if (lane < kWaves) wsum[lane] = wi - w;
+        if (lane == kWaves - 1) *total = wi;
+    }
+    __syncthreads();
+    const uint32_t r = wsum[wave] + incl - v;
+    __syncthreads();
+    return r;
+}
+
+// Radix keys of keys base + j*kSelThreads + t (j < kSelUnroll) into
+// registers; every load is issued before any is used.  Keys at or past s1 are
+// not read (their slot gets key 0; callers test the position).
+__device__ __forceinline__ void load_keys(const float *row, int64_t base, int64_t s1,
                                           uint32_t (&u)[kSelUnroll]) {
     const int t = threadIdx.x;
     float v[kSelUnroll];
@@ -84,100 +131,22 @@ __device__ __forceinline__ void load_tile(const float *row, int64_t base, int64_
     for (int j = 0; j < kSelUnroll; ++j) u[j] = radix_key(v[j]);
 }
 
-template <typename T>
-__device__ __forceinline__ T tmin(T a, T b) { return a < b ? a : b; }
-template <typename T>
-__device__ __forceinline__ T tmax(T a, T b) { return a < b ? b : a; }
-
-// Bitonic sort of n = kSelThreads * EPT values, thread t holding elements
-// t*EPT + e in x[e].  Partners inside a thread are compared in registers,
-// partners inside a wave are fetched with a lane shuffle, and only partners
-// in another wave go through LDS (`lds`: n values of scratch).
-template <typename T, int EPT, bool kAsc>
-__device__ void block_sort(T (&x)[EPT], T *lds) {
+// Bitonic sort of v[0..n) in LDS (n a power of two <= 4096), runtime loops.
+template <typename T, bool kAsc>
+__device__ void lds_bitonic(T *v, int n) {
     const int t = threadIdx.x;
-    constexpr int n = kSelThreads * EPT;
-#pragma unroll
     for (int kk = 2; kk <= n; kk <<= 1) {
-#pragma unroll
         for (int j = kk >> 1; j > 0; j >>= 1) {
-            if (j < EPT) {
-#pragma unroll
-                for (int e = 0; e < EPT; ++e) {
-                    const int e2 = e ^ j;
-                    if (e2 > e) {
-                        const int i = t * EPT + e;
-                        const bool up = ((i & kk) == 0) == kAsc;
-                        const T a = x[e], b = x[e2];
-                        x[e] = up ? tmin(a, b) : tmax(a, b);
-                        x[e2] = up ? tmax(a, b) : tmin(a, b);
-                    }
-                }
-            } else if (j < EPT * 64) {
-#pragma unroll
-                for (int e = 0; e < EPT; ++e) {
-                    const int i = t * EPT + e;
-                    const T y = __shfl_xor(x[e], j / EPT);
-                    const bool keep_min = (((i & j) == 0) == (((i & kk) == 0) == kAsc));
-                    x[e] = keep_min ? tmin(x[e], y) : tmax(x[e], y);
-                }
-            } else {
-                __syncthreads();
-#pragma unroll
-                for (int e = 0; e < EPT; ++e) lds[t * EPT + e] = x[e];
-                __syncthreads();
-#pragma unroll
-                for (int e = 0; e < EPT; ++e) {
-                    const int i = t * EPT + e;
-                    const T y = lds[i ^ j];
-                    const bool keep_min = (((i & j) == 0) == (((i & kk) == 0) == kAsc));
-                    x[e] = keep_min ? tmin(x[e], y) : tmax(x[e], y);
-                }
+            for (int i = t; i < n / 2; i += kSelThreads) {
+                const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+                const int hi = lo + j;
+                const bool up = ((lo & kk) == 0) == kAsc;
+                const T x = v[lo], y = v[hi];
+                if (up ? (x > y) : (x < y)) { v[lo] = y; v[hi] = x; }
             }
+            __syncthreads();
         }
     }
-    __syncthreads();
-}
-
-
-// The `need` largest candidates (key << 32 | ~index, so equal keys order by
-// lower index): their indices land in ch[0..need) in no particular order.
-template <int EPT>
-__device__ void take_candidates(const unsigned long long *cand, uint32_t n_cand, uint32_t need,
-                                int32_t *ch, unsigned long long *lds) {
-    const int t = threadIdx.x;
-    unsigned long long x[EPT];
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-        const uint32_t i = t * EPT + e;
-        x[e] = i < n_cand ? cand[i] : 0ull;
-    }
-    block_sort<unsigned long long, EPT, false>(x, lds);
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-        const uint32_t i = t * EPT + e;
-        if (i < need) ch[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(x[e] & 0xFFFFFFFFull));
-    }
-    __syncthreads();
-}
-
-// v[0..n) sorted ascending in place (n <= kSelThreads * EPT).
-template <int EPT>
-__device__ void sort_small(int32_t *v, int n, int32_t *lds) {
-    const int t = threadIdx.x;
-    int32_t x[EPT];
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-        const int i = t * EPT + e;
-        x[e] = i < n ? v[i] : 0x7FFFFFFF;
-    }
-    block_sort<int32_t, EPT, true>(x, lds);
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-        const int i = t * EPT + e;
-        if (i < n) v[i] = x[e];
-    }
-    __syncthreads();
 }
 
 __device__ __forceinline__ int lower_bound(const int32_t *a, int n, int32_t v) {
@@ -189,77 +158,200 @@ __device__ __forceinline__ int lower_bound(const int32_t *a, int n, int32_t v) {
     return lo;
 }
 
+// Last slice x in [0, n) whose offset off[x] is <= p.
+__device__ __forceinline__ int slice_of(const uint32_t *off, int n, uint32_t p) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= p) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
 __device__ __forceinline__ int clamp_bound(int b, int max_bound) {
     return b < 0 ? 0 : (b > max_bound ? max_bound : b);
 }
 
 // ---------------------------------------------------------------- hist1
 // First-digit histogram of stored scores (used when the scores were not
-// produced by this launch's scoring pass).
+// produced by this launch's scoring pass).  One LDS copy per wave.
 __global__ __launch_bounds__(kSelThreads) void hist1_kernel(SelectArgs a) {
-    __shared__ uint32_t h[kBins1];
-    const int r = blockIdx.y, t = threadIdx.x;
+    __shared__ uint32_t h[kWaves][kBins1];
+    const int r = blockIdx.y, t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int b = clamp_bound(a.row_bound[r], a.max_bound);
     const int64_t s0 = (int64_t)blockIdx.x * a.L.sel_chunk;
     if (s0 >= b) return;
     const int64_t s1 = min(s0 + a.L.sel_chunk, (int64_t)b);
-    if (t < kBins1) h[t] = 0;
-    __syncthreads();
     const float *row = a.scores + (int64_t)r * a.sstride;
+    uint32_t u[kSelUnroll];
+    load_keys(row, s0, s1, u);
+    h[wave][lane] = 0;
+    __syncthreads();
     for (int64_t base = s0; base < s1; base += kSelTile) {
-        uint32_t u[kSelUnroll];
-        load_tile(row, base, s1, u);
+        if (base != s0) load_keys(row, base, s1, u);
 #pragma unroll
         for (int j = 0; j < kSelUnroll; ++j)
-            if (base + j * kSelThreads + t < s1) atomicAdd(&h[u[j] >> kDigit1Shift], 1u);
+            if (base + j * kSelThreads + t < s1) atomicAdd(&h[wave][u[j] >> kDigit1Shift], 1u);
     }
     __syncthreads();
-    uint32_t *hist1 = (uint32_t *)(a.ws + a.L.hist1);
-    if (t < kBins1 && h[t]) atomicAdd(hist1 + (int64_t)r * kBins1 + t, h[t]);
+    if (t < kBins1) {
+        uint32_t c = 0;
+        for (int w = 0; w < kWaves; ++w) c += h[w][t];
+        if (c) atomicAdd((uint32_t *)(a.ws + a.L.hist1) + (int64_t)r * kBins1 + t, c);
+    }
 }
 
 // ---------------------------------------------------------------- refine
 // Second-digit counts inside the first-digit bin of the k-th largest key.
+// One LDS copy per wave keeps the waves' atomics off each other's words.
 __global__ __launch_bounds__(kSelThreads) void refine_kernel(SelectArgs a) {
     __shared__ uint32_t h1[kBins1];
-    __shared__ uint32_t h2[kBins2];
+    __shared__ uint32_t h2[kWaves][kBins2];
     __shared__ int sb1;
     __shared__ uint32_t sabove1;
-    const int r = blockIdx.y, x = blockIdx.x, t = threadIdx.x, lane = t & 63;
+    const int r = blockIdx.y, x = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int b = clamp_bound(a.row_bound[r], a.max_bound);
     const uint32_t k = (uint32_t)a.topk;
     const int64_t s0 = (int64_t)x * a.L.sel_chunk;
     if ((uint32_t)b <= k || s0 >= b) return;   // all selected, or nothing here
     const int64_t s1 = min(s0 + a.L.sel_chunk, (int64_t)b);
-    const uint32_t *hist1 = (const uint32_t *)(a.ws + a.L.hist1) + (int64_t)r * kBins1;
-    uint32_t *hist2 = (uint32_t *)(a.ws + a.L.hist2) + (int64_t)r * kBins2;
     const float *row = a.scores + (int64_t)r * a.sstride;
 
     uint32_t u[kSelUnroll];
-    load_tile(row, s0, s1, u);   // first step's loads overlap the digit search
-    if (t < kBins1) h1[t] = hist1[t];
-    h2[t] = 0;
+    load_keys(row, s0, s1, u);   // the first step's loads overlap the digit search
+    if (t < kBins1) h1[t] = ((const uint32_t *)(a.ws + a.L.hist1))[(int64_t)r * kBins1 + t];
+    for (int i = t; i < kWaves * kBins2; i += kSelThreads) (&h2[0][0])[i] = 0;
     if (t == 0) { sb1 = 0; sabove1 = 0; }
     __syncthreads();
     if (t < 64) wave_find_bin(h1, 1, k, lane, &sb1, &sabove1);
     __syncthreads();
     const uint32_t b1 = (uint32_t)sb1;
     for (int64_t base = s0; base < s1; base += kSelTile) {
-        if (base != s0) load_tile(row, base, s1, u);
+        if (base != s0) load_keys(row, base, s1, u);
 #pragma unroll
         for (int j = 0; j < kSelUnroll; ++j)
             if (base + j * kSelThreads + t < s1 && (u[j] >> kDigit1Shift) == b1)
-                atomicAdd(&h2[(u[j] >> kDigit2Shift) & (kBins2 - 1)], 1u);
+                atomicAdd(&h2[wave][(u[j] >> kDigit2Shift) & (kBins2 - 1)], 1u);
     }
     __syncthreads();
-    if (h2[t]) atomicAdd(hist2 + t, h2[t]);
+    if (t < kBins2) {
+        uint32_t c = 0;
+        for (int w = 0; w < kWaves; ++w) c += h2[w][t];
+        if (c) atomicAdd((uint32_t *)(a.ws + a.L.hist2) + (int64_t)r * kBins2 + t, c);
+    }
+}
+
+// ---------------------------------------------------------------- gather
+// Every workgroup of a row derives the same split from the two histograms,
+// writes its sure keys and candidates (each ascending) to its own slices and
+// counts the candidates' third digits.
+__global__ __launch_bounds__(kSelThreads) void gather_kernel(SelectArgs a) {
+    __shared__ uint32_t h1[kBins1];
+    __shared__ uint32_t h2[kBins2];
+    __shared__ uint32_t h3[kBins3];
+    __shared__ uint32_t cs[kSelUnroll * kWaves], cc[kSelUnroll * kWaves];
+    __shared__ int sb1, sb2;
+    __shared__ uint32_t sabove1, sabove2, tot_s, tot_c;
+    const int r = blockIdx.y, x = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int b = clamp_bound(a.row_bound[r], a.max_bound);
+    const int k = a.topk;
+    const int S = a.L.sel_wgs;
+    int32_t *out_row = a.out_idx + (int64_t)r * k;
+    if (b <= k) {   // every key selected: indices 0..b-1, then -1
+        if (x == 0)
+            for (int i = t; i < k; i += kSelThreads) out_row[i] = i < b ? i : -1;
+        return;
+    }
+    int32_t *slice_s = (int32_t *)(a.ws + a.L.sure_list) + ((int64_t)r * S + x) * kMaxTopk;
+    unsigned long long *slice_c = (unsigned long long *)(a.ws + a.L.cand_list) + ((int64_t)r * S + x) * kCandSlice;
+    const float *row = a.scores + (int64_t)r * a.sstride;
+    const int64_t s0 = (int64_t)x * a.L.sel_chunk;
+    const int64_t s1 = min(s0 + a.L.sel_chunk, (int64_t)b);
+
+    uint32_t u[kSelUnroll];
+    if (s0 < s1) load_keys(row, s0, s1, u);   // overlaps the split below
+    // ---- the split: (b1, above1) from the first digit, (b2, above2) from the second
+    if (t < kBins1) h1[t] = ((const uint32_t *)(a.ws + a.L.hist1))[(int64_t)r * kBins1 + t];
+    if (t < kBins2) {
+        h2[t] = ((const uint32_t *)(a.ws + a.L.hist2))[(int64_t)r * kBins2 + t];
+        h3[t] = 0;
+    }
+    if (t == 0) { sb1 = 0; sabove1 = 0; sb2 = 0; sabove2 = 0; }
+    __syncthreads();
+    if (t < 64) wave_find_bin(h1, 1, (uint32_t)k, lane, &sb1, &sabove1);
+    __syncthreads();
+    if (t < 64) wave_find_bin(h2, kBins2 / 64, (uint32_t)k - sabove1, lane, &sb2, &sabove2);
+    __syncthreads();
+    const uint32_t b1 = (uint32_t)sb1, b2 = (uint32_t)sb2;
+    const uint32_t T14 = (b1 << kDigit2Bits) | b2;
+    if (x == 0 && t == 0) {
+        RowState st;
+        st.b1 = b1;
+        st.b2 = b2;
+        st.sure = sabove1 + sabove2;
+        st.need = (uint32_t)k - st.sure;
+        st.cand = h2[b2];
+        st.pad[0] = st.pad[1] = st.pad[2] = 0;
+        ((RowState *)(a.ws + a.L.state))[r] = st;
+    }
+
+    uint32_t ws_ = 0, wc_ = 0;   // sure keys / candidates of this workgroup so far
+    for (int64_t base = s0; base < s1; base += kSelTile) {
+        if (base != s0) load_keys(row, base, s1, u);
+        // pass 1: counts per (step j, wave), in key order; third digits of candidates
+#pragma unroll
+        for (int j = 0; j < kSelUnroll; ++j) {
+            const bool valid = base + j * kSelThreads + t < s1;
+            const uint32_t top = u[j] >> kDigit2Shift;
+            const bool sure = valid && top > T14;
+            const bool cnd = valid && top == T14;
+            const uint64_t ms = __ballot(sure);
+            const uint64_t mc = __ballot(cnd);
+            if (lane == 0) {
+                cs[j * kWaves + wave] = (uint32_t)__popcll(ms);
+                cc[j * kWaves + wave] = (uint32_t)__popcll(mc);
+            }
+            if (cnd) atomicAdd(&h3[(u[j] >> kDigit3Shift) & (kBins3 - 1)], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) wave_scan128(cs, &tot_s, lane);
+        if (wave == 1) wave_scan128(cc, &tot_c, lane);
+        __syncthreads();
+        // pass 2: each key to its place
+#pragma unroll
+        for (int j = 0; j < kSelUnroll; ++j) {
+            const int64_t s = base + j * kSelThreads + t;
+            const bool valid = s < s1;
+            const uint32_t top = u[j] >> kDigit2Shift;
+            const bool sure = valid && top > T14;
+            const bool cnd = valid && top == T14;
+            const uint64_t ms = __ballot(sure);
+            const uint64_t mc = __ballot(cnd);
+            if (sure) {
+                const uint32_t pos = ws_ + cs[j * kWaves + wave] + lane_prefix(ms);
+                if (pos < (uint32_t)kMaxTopk) slice_s[pos] = (int32_t)s;
+            }
+            if (cnd) {
+                const uint32_t pos = wc_ + cc[j * kWaves + wave] + lane_prefix(mc);
+                if (pos < (uint32_t)kCandSlice) slice_c[pos] = ((unsigned long long)u[j] << 32) | (uint32_t)s;
+            }
+        }
+        ws_ += tot_s;
+        wc_ += tot_c;
+        __syncthreads();
+    }
+    if (t == 0) {
+        ((uint32_t *)(a.ws + a.L.sure_cnt))[(int64_t)r * S + x] = ws_ < (uint32_t)kMaxTopk ? ws_ : (uint32_t)kMaxTopk;
+        ((uint32_t *)(a.ws + a.L.cand_cnt))[(int64_t)r * S + x] = wc_;
+    }
+    if (t < kBins3 && h3[t]) atomicAdd((uint32_t *)(a.ws + a.L.hist3) + (int64_t)r * kBins3 + t, h3[t]);
 }
 
 // ------------------------------------------------------------- fallback
-// Exact resolution inside the 14-bit prefix bin by one workgroup, used when
-// the bin holds more than kCandCap keys: three more digit passes fix the
-// threshold key T, then keys above T and the first `need - above` ties at T
-// in index order go to ch[0..need) (in no particular order).
+// Exact resolution inside the 14-bit prefix bin by one workgroup rescanning
+// the row, used when the candidates overflow their slices: three more digit
+// passes fix the threshold key T, then keys above T and the first
+// `need - above` ties at T in index order go to ch[0..need) (any order).
 __device__ void fallback_select(const float *row, int b, uint32_t T14, uint32_t need, int32_t *ch,
                                 uint32_t *h, int *sB, uint32_t *sAbove, uint32_t *wtot, uint32_t *spos) {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -269,14 +361,14 @@ __device__ void fallback_select(const float *row, int b, uint32_t T14, uint32_t 
     int pshift = kDigit2Shift;
     uint32_t need_cur = need;
     for (int d = 0; d < 3; ++d) {
-        h[t] = 0;
+        if (t < kBins2) h[t] = 0;
         if (t == 0) { *sB = 0; *sAbove = 0; }
         __syncthreads();
         const uint32_t mask = (1u << widths[d]) - 1u;
         const int sh = shifts[d];
         for (int64_t base = 0; base < b; base += kSelTile) {
             uint32_t u[kSelUnroll];
-            load_tile(row, base, b, u);
+            load_keys(row, base, b, u);
 #pragma unroll
             for (int j = 0; j < kSelUnroll; ++j)
                 if (base + j * kSelThreads + t < b && (u[j] >> pshift) == prefix)
@@ -304,7 +396,7 @@ __device__ void fallback_select(const float *row, int b, uint32_t T14, uint32_t 
         if (lane == 0) wtot[wave] = (uint32_t)__popcll(m);
         __syncthreads();
         uint32_t woff = 0, all = 0;
-        for (int wv = 0; wv < kSelThreads / 64; ++wv) {
+        for (int wv = 0; wv < kWaves; ++wv) {
             if (wv < wave) woff += wtot[wv];
             all += wtot[wv];
         }
@@ -318,199 +410,140 @@ __device__ void fallback_select(const float *row, int b, uint32_t T14, uint32_t 
     }
 }
 
-// ---------------------------------------------------------------- gather
-// Every workgroup of a row derives the same split from the two histograms,
-// writes its sure keys (ascending) to its own slice and appends candidates.
-__global__ __launch_bounds__(kSelThreads) void gather_kernel(SelectArgs a) {
-    __shared__ unsigned long long l_cand[kCandCap];
-    __shared__ uint32_t h1[kBins1];
-    __shared__ uint32_t h2[kBins2];
-    __shared__ uint32_t cnt[kSelUnroll * (kSelThreads / 64)];
-    __shared__ int sb1, sb2;
-    __shared__ uint32_t sabove1, sabove2, n_cand_l, g_cand, tile_total;
-    const int r = blockIdx.y, x = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int b = clamp_bound(a.row_bound[r], a.max_bound);
-    const int k = a.topk;
-    const int S = a.L.sel_wgs;
-    int32_t *out_row = a.out_idx + (int64_t)r * k;
-    if (b <= k) {   // every key selected: indices 0..b-1, then -1
-        if (x == 0)
-            for (int i = t; i < k; i += kSelThreads) out_row[i] = i < b ? i : -1;
-        return;
-    }
-    const uint32_t *hist1 = (const uint32_t *)(a.ws + a.L.hist1) + (int64_t)r * kBins1;
-    const uint32_t *hist2 = (const uint32_t *)(a.ws + a.L.hist2) + (int64_t)r * kBins2;
-    uint32_t *cand_slot = (uint32_t *)(a.ws + a.L.cand_slot) + r;
-    unsigned long long *cand = (unsigned long long *)(a.ws + a.L.cand) + (int64_t)r * kCandCap;
-    int32_t *slice = (int32_t *)(a.ws + a.L.sure_list) + ((int64_t)r * S + x) * kMaxTopk;
-    const float *row = a.scores + (int64_t)r * a.sstride;
-    const int64_t s0 = (int64_t)x * a.L.sel_chunk;
-    const int64_t s1 = min(s0 + a.L.sel_chunk, (int64_t)b);
-
-    uint32_t u[kSelUnroll];
-    if (s0 < s1) load_tile(row, s0, s1, u);   // overlaps the split below
-    // ---- the split: (b1, above1) from the first digit, (b2, above2) from the second
-    if (t < kBins1) h1[t] = hist1[t];
-    h2[t] = hist2[t];
-    if (t == 0) { sb1 = 0; sabove1 = 0; sb2 = 0; sabove2 = 0; n_cand_l = 0; }
-    __syncthreads();
-    if (t < 64) wave_find_bin(h1, 1, (uint32_t)k, lane, &sb1, &sabove1);
-    __syncthreads();
-    if (t < 64) wave_find_bin(h2, kBins2 / 64, (uint32_t)k - sabove1, lane, &sb2, &sabove2);
-    __syncthreads();
-    const uint32_t b1 = (uint32_t)sb1, b2 = (uint32_t)sb2;
-    const uint32_t T14 = (b1 << kDigit2Bits) | b2;
-    if (x == 0 && t == 0) {
-        RowState st;
-        st.b1 = b1;
-        st.b2 = b2;
-        st.sure = sabove1 + sabove2;
-        st.need = (uint32_t)k - st.sure;
-        st.cand = h2[b2];
-        st.pad[0] = st.pad[1] = st.pad[2] = 0;
-        ((RowState *)(a.ws + a.L.state))[r] = st;
-    }
-
-    uint32_t written = 0;   // sure keys of this workgroup so far (uniform)
-    for (int64_t base = s0; base < s1; base += kSelTile) {
-        if (base != s0) load_tile(row, base, s1, u);
-        // pass 1: sure keys per (step j, wave); candidates to the LDS list
-#pragma unroll
-        for (int j = 0; j < kSelUnroll; ++j) {
-            const bool valid = base + j * kSelThreads + t < s1;
-            const uint32_t top = u[j] >> kDigit2Shift;
-            const uint64_t ms = __ballot(valid && top > T14);
-            if (lane == 0) cnt[j * 4 + wave] = (uint32_t)__popcll(ms);
-            const bool cnd = valid && top == T14;
-            const uint64_t mc = __ballot(cnd);
-            if (mc) {
-                uint32_t pos0 = 0;
-                if (lane == 0) pos0 = atomicAdd(&n_cand_l, (uint32_t)__popcll(mc));
-                pos0 = __shfl(pos0, 0);
-                const uint32_t pos = pos0 + lane_prefix(mc);
-                const int64_t s = base + j * kSelThreads + t;
-                if (cnd && pos < (uint32_t)kCandCap)
-                    l_cand[pos] = ((unsigned long long)u[j] << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)s);
-            }
-        }
-        __syncthreads();
-        // exclusive prefix of the 128 counts, in key order (step-major, then wave)
-        if (t < 64) {
-            const uint32_t c0 = cnt[2 * lane], c1 = cnt[2 * lane + 1];
-            uint32_t incl = c0 + c1;
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t v = __shfl_up(incl, off);
-                if (lane >= off) incl += v;
-            }
-            const uint32_t excl = incl - c0 - c1;
-            cnt[2 * lane] = excl;
-            cnt[2 * lane + 1] = excl + c0;
-            if (lane == 63) tile_total = incl;
-        }
-        __syncthreads();
-        // pass 2: each sure key to its place
-#pragma unroll
-        for (int j = 0; j < kSelUnroll; ++j) {
-            const bool valid = base + j * kSelThreads + t < s1;
-            const bool sure = valid && (u[j] >> kDigit2Shift) > T14;
-            const uint64_t ms = __ballot(sure);
-            if (sure) {
-                const uint32_t pos = written + cnt[j * 4 + wave] + lane_prefix(ms);
-                if (pos < (uint32_t)kMaxTopk) slice[pos] = (int32_t)(base + j * kSelThreads + t);
-            }
-        }
-        written += tile_total;
-        __syncthreads();
-    }
-    if (t == 0) {
-        ((uint32_t *)(a.ws + a.L.sure_cnt))[(int64_t)r * S + x] = written < (uint32_t)kMaxTopk ? written : (uint32_t)kMaxTopk;
-        g_cand = n_cand_l ? atomicAdd(cand_slot, n_cand_l) : 0u;
-    }
-    __syncthreads();
-    const uint32_t nc = min(n_cand_l, (uint32_t)kCandCap);
-    for (uint32_t i = t; i < nc; i += kSelThreads)
-        if (g_cand + i < (uint32_t)kCandCap) cand[g_cand + i] = l_cand[i];
-}
-
 // -------------------------------------------------------------- finalize
 // One workgroup per row: choose the `need` candidates, merge them with the
 // sure keys into the row's output in ascending index order, and leave the
-// row's histograms and candidate counter zeroed.
+// row's histograms zeroed.
 __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
-    __shared__ unsigned long long sortbuf[kCandCap];
-    __shared__ int32_t su[kMaxTopk];
-    __shared__ int32_t ch[kMaxTopk];
-    __shared__ uint32_t off[kSelMaxWgs + 1];
-    __shared__ uint32_t h[kBins2];
-    __shared__ uint32_t wtot[kSelThreads / 64];
+    __shared__ unsigned long long tie[kTieCap];   // candidates inside the third-digit bin
+    __shared__ int32_t su[kMaxTopk];              // sure keys, ascending
+    __shared__ int32_t chs[kMaxTopk];             // chosen candidates, ascending
+    __shared__ uint32_t offs[kSelMaxWgs + 1], offc[kSelMaxWgs + 1];
+    __shared__ uint32_t h3[kBins3];
+    __shared__ uint32_t wsum[kWaves];
     __shared__ int sB;
-    __shared__ uint32_t sAbove, spos;
-    const int r = blockIdx.x, t = threadIdx.x, lane = t & 63;
+    __shared__ uint32_t sAbove, ntie, ovf, total, spos;
+    const int r = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int b = clamp_bound(a.row_bound[r], a.max_bound);
     const int k = a.topk;
     const int S = a.L.sel_wgs;
     int32_t *out_row = a.out_idx + (int64_t)r * k;
+    uint32_t *hist3 = (uint32_t *)(a.ws + a.L.hist3) + (int64_t)r * kBins3;
     if (b > k) {
         const RowState st = ((const RowState *)(a.ws + a.L.state))[r];
-        const unsigned long long *cand = (const unsigned long long *)(a.ws + a.L.cand) + (int64_t)r * kCandCap;
-        const uint32_t *cnts = (const uint32_t *)(a.ws + a.L.sure_cnt) + (int64_t)r * S;
-        const int32_t *slices = (const int32_t *)(a.ws + a.L.sure_list) + (int64_t)r * S * kMaxTopk;
-        const float *row = a.scores + (int64_t)r * a.sstride;
-        // slice offsets: exclusive prefix of the per-workgroup sure counts
-        if (t < 64) {
-            const uint32_t c = lane < S ? cnts[lane] : 0u;
+        const uint32_t *scnt = (const uint32_t *)(a.ws + a.L.sure_cnt) + (int64_t)r * S;
+        const uint32_t *ccnt = (const uint32_t *)(a.ws + a.L.cand_cnt) + (int64_t)r * S;
+        const int32_t *sl_s = (const int32_t *)(a.ws + a.L.sure_list) + (int64_t)r * S * kMaxTopk;
+        const unsigned long long *sl_c = (const unsigned long long *)(a.ws + a.L.cand_list) + (int64_t)r * S * kCandSlice;
+        const int need = (int)(st.need < (uint32_t)kMaxTopk ? st.need : (uint32_t)kMaxTopk);
+        const uint32_t T14 = (st.b1 << kDigit2Bits) | st.b2;
+        // slice offsets (exclusive prefix of the per-workgroup counts)
+        if (wave < 2) {
+            const uint32_t c = lane < S ? (wave == 0 ? scnt[lane] : ccnt[lane]) : 0u;
+            const uint64_t big = __ballot(wave == 1 && c > (uint32_t)kCandSlice);
             uint32_t incl = c;
             for (int o = 1; o < 64; o <<= 1) {
                 const uint32_t v = __shfl_up(incl, o);
                 if (lane >= o) incl += v;
             }
+            uint32_t *off = wave == 0 ? offs : offc;
             off[lane] = incl - c;
-            if (lane == 63) off[kSelMaxWgs] = incl;
-        }
-        // the candidates to take
-        const uint32_t need = st.need < (uint32_t)kMaxTopk ? st.need : (uint32_t)kMaxTopk;
-        const uint32_t n_cand = st.cand;
-        if (n_cand <= (uint32_t)kCandCap) {
-            if (n_cand <= 256) take_candidates<1>(cand, n_cand, need, ch, sortbuf);
-            else if (n_cand <= 512) take_candidates<2>(cand, n_cand, need, ch, sortbuf);
-            else if (n_cand <= 1024) take_candidates<4>(cand, n_cand, need, ch, sortbuf);
-            else if (n_cand <= 2048) take_candidates<8>(cand, n_cand, need, ch, sortbuf);
-            else take_candidates<16>(cand, n_cand, need, ch, sortbuf);
-        } else {
-            fallback_select(row, b, (st.b1 << kDigit2Bits) | st.b2, need, ch, h, &sB, &sAbove, wtot, &spos);
-        }
-        __syncthreads();
-        int32_t *scratch = (int32_t *)sortbuf;
-        if (need <= 256) sort_small<1>(ch, need, scratch);
-        else if (need <= 512) sort_small<2>(ch, need, scratch);
-        else if (need <= 1024) sort_small<4>(ch, need, scratch);
-        else sort_small<8>(ch, need, scratch);
-        // the sure keys: slices concatenated in workgroup order are ascending
-        const int ns = (int)min(off[kSelMaxWgs], (uint32_t)k - need);
-        for (int p = t; p < ns; p += kSelThreads) {
-            int lo = 0, hi = S - 1;   // last slice whose offset is <= p
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (off[mid] <= (uint32_t)p) lo = mid; else hi = mid - 1;
+            if (lane == 63) {
+                off[kSelMaxWgs] = incl;
+                if (wave == 1) ovf = (big != 0ull) || incl > (uint32_t)kCandCap;
             }
-            su[p] = slices[(int64_t)lo * kMaxTopk + (p - (int)off[lo])];
+        }
+        if (t < kBins3) h3[t] = hist3[t];
+        if (t == 0) { sB = 0; sAbove = 0; ntie = 0; }
+        __syncthreads();
+        const int ns = (int)min(offs[kSelMaxWgs], (uint32_t)(k - need));
+        const int nc = (int)offc[kSelMaxWgs];
+        bool overflow = ovf != 0u;
+        // the sure keys: slices concatenated in workgroup order are ascending
+        {
+            int32_t v0 = 0, v1 = 0;
+            const int p0 = t, p1 = t + kSelThreads;
+            if (p0 < ns) { const int xs = slice_of(offs, S, p0); v0 = sl_s[(int64_t)xs * kMaxTopk + (p0 - (int)offs[xs])]; }
+            if (p1 < ns) { const int xs = slice_of(offs, S, p1); v1 = sl_s[(int64_t)xs * kMaxTopk + (p1 - (int)offs[xs])]; }
+            if (p0 < ns) su[p0] = v0;
+            if (p1 < ns) su[p1] = v1;
+        }
+        unsigned long long c[4];
+        if (!overflow) {
+            // this thread's candidates t*4 .. t*4+3 (ascending index)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = t * 4 + q;
+                c[q] = 0ull;
+                if (i < nc) { const int xc = slice_of(offc, S, i); c[q] = sl_c[(int64_t)xc * kCandSlice + (i - (int)offc[xc])]; }
+            }
+            if (t < 64) wave_find_bin(h3, kBins3 / 64, (uint32_t)need, lane, &sB, &sAbove);
+            __syncthreads();
+            const uint32_t T22 = (T14 << kDigit3Bits) | (uint32_t)sB;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (t * 4 + q < nc && (uint32_t)(c[q] >> (32 + kDigit3Shift)) == T22) {
+                    const uint32_t p = atomicAdd(&ntie, 1u);
+                    if (p < (uint32_t)kTieCap) tie[p] = c[q];
+                }
+            }
+            __syncthreads();
+            overflow = ntie > (uint32_t)kTieCap;
+        }
+        if (!overflow) {
+            const uint32_t T22 = (T14 << kDigit3Bits) | (uint32_t)sB;
+            const uint32_t need3 = (uint32_t)need - sAbove;
+            const int nt = (int)ntie;
+            bool chosen[4];
+            uint32_t cnt = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                chosen[q] = false;
+                if (t * 4 + q < nc) {
+                    const uint32_t key = (uint32_t)(c[q] >> 32);
+                    const uint32_t d = key >> kDigit3Shift;
+                    if (d > T22) {
+                        chosen[q] = true;
+                    } else if (d == T22) {   // rank inside the bin: larger key first, then lower index
+                        const uint32_t idx = (uint32_t)c[q];
+                        uint32_t rank = 0;
+                        for (int e = 0; e < nt; ++e) {
+                            const uint32_t ek = (uint32_t)(tie[e] >> 32), ei = (uint32_t)tie[e];
+                            rank += (ek > key) || (ek == key && ei < idx);
+                        }
+                        chosen[q] = rank < need3;
+                    }
+                }
+                cnt += chosen[q];
+            }
+            uint32_t pos = block_scan(cnt, wsum, &total);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (chosen[q] && pos < (uint32_t)kMaxTopk) chs[pos++] = (int32_t)(uint32_t)c[q];
+        } else {
+            fallback_select(a.scores + (int64_t)r * a.sstride, b, T14, (uint32_t)need, chs, h3, &sB,
+                            &sAbove, wsum, &spos);
+            __syncthreads();
+            int n2 = 1;
+            while (n2 < need) n2 <<= 1;
+            for (int i = need + t; i < n2; i += kSelThreads) chs[i] = 0x7FFFFFFF;
+            __syncthreads();
+            lds_bitonic<int32_t, true>(chs, n2);
         }
         __syncthreads();
         // merge: each value's place is its rank in its own list plus its rank in the other
         for (int p = t; p < ns; p += kSelThreads) {
             const int32_t v = su[p];
-            out_row[p + lower_bound(ch, (int)need, v)] = v;
+            out_row[p + lower_bound(chs, need, v)] = v;
         }
-        for (int j = t; j < (int)need; j += kSelThreads) {
-            const int32_t c = ch[j];
-            out_row[j + lower_bound(su, ns, c)] = c;
+        for (int j = t; j < need; j += kSelThreads) {
+            const int32_t cj = chs[j];
+            out_row[j + lower_bound(su, ns, cj)] = cj;
         }
     }
-    uint32_t *hist1 = (uint32_t *)(a.ws + a.L.hist1) + (int64_t)r * kBins1;
-    uint32_t *hist2 = (uint32_t *)(a.ws + a.L.hist2) + (int64_t)r * kBins2;
-    if (t < kBins1) hist1[t] = 0;
-    hist2[t] = 0;
-    if (t == 0) ((uint32_t *)(a.ws + a.L.cand_slot))[r] = 0;
+    if (t < kBins1) ((uint32_t *)(a.ws + a.L.hist1))[(int64_t)r * kBins1 + t] = 0;
+    if (t < kBins2) ((uint32_t *)(a.ws + a.L.hist2))[(int64_t)r * kBins2 + t] = 0;
+    if (t < kBins3) hist3[t] = 0;
 }
 
 __global__ void fill_zero_kernel(uint32_t *p, size_t n) {
