@@ -16,6 +16,8 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     # keep packed fp32 VALU ops out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the epilogue reads them directly, no AGPR copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

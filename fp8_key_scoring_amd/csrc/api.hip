@@ -57,7 +57,7 @@ int score_chunk(const fp8idx_problem_t *p) {
     int64_t ch = groups * (int64_t)p->max_bound / 512;
     ch = (ch + 63) / 64 * 64;
     if (ch < 256) ch = 256;
-    if (ch > 8192) ch = 8192;
+    if (ch > 4096) ch = 4096;   // the score kernel keeps a chunk's <= 64 page ids in one VGPR
     return (int)ch;
 }
 
