@@ -52,9 +52,9 @@ int check_device() {
 }
 
 int score_chunk(const fp8idx_problem_t *p) {
-    // aim at about two workgroups per CU on the longest request group
+    // aim at about one workgroup per CU (256 CUs) on the longest request group
     const int64_t groups = (p->rows + kGroupRows - 1) / kGroupRows;
-    int64_t ch = groups * (int64_t)p->max_bound / 512;
+    int64_t ch = groups * (int64_t)p->max_bound / 256;
     ch = (ch + 63) / 64 * 64;
     if (ch < 256) ch = 256;
     if (ch > 4096) ch = 4096;   // the score kernel keeps a chunk's <= 64 page ids in one VGPR

@@ -72,25 +72,12 @@ __device__ __forceinline__ float lane_sum_64(float v) {
     return __int_as_float(q[0]) + __int_as_float(q[1]);
 }
 
-// Adds one to bin d of an LDS histogram for every lane with valid set.  Scores
-// of one row mostly share a first digit, so per-lane atomics would pile onto
-// one LDS address; the two most common bins of the wave are added once each
-// (ballot + popcount) and only the remaining lanes add one by one.
-__device__ __forceinline__ void count_digit1(uint32_t *hist, uint32_t d, bool valid, int lane) {
-    bool pending = valid;
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const uint64_t act = __ballot(pending);
-        if (act == 0) return;
-        const int leader = __ffsll((unsigned long long)act) - 1;
-        const uint32_t d0 = __builtin_amdgcn_readlane(d, leader);
-        const bool mine = pending && d == d0;
-        const uint64_t m = __ballot(mine);
-        if (lane == leader) atomicAdd(&hist[d0], (uint32_t)__popcll(m));
-        pending = pending && !mine;
-    }
-    if (pending) atomicAdd(&hist[d], 1u);
-}
+// First-digit counters in LDS: [row slot][digit][64], one counter per lane
+// and digit, at position (lane + digit) % 64.  A wave's scores share only a
+// handful of first digits, so one counter per digit would make the lanes of
+// an atomic add collide; with the skew every lane of one add hits its own
+// bank, and the reduction (lane = digit, summing its 64 counters) does too.
+constexpr int kHistLds = kGroupRows * kBins1 * 64;   // u32 counters
 
 struct KeyGroup {
     u32x4_t lo, hi;   // 32 code bytes of key lane%16
@@ -98,10 +85,189 @@ struct KeyGroup {
     int ok;           // wave-uniform: the page id was in range
 };
 
+// What one wave scores: R rows (R = 1 or 2) over every parts-th 16-key group
+// of the chunk, starting at group g_first.
+struct WaveJob {
+    int lane;
+    int c0;          // first key of the chunk (a multiple of 64)
+    int chunk;       // keys per chunk (row stride of the LDS score buffer)
+    int g_first;     // first 16-key group (index over the request's keys)
+    int parts;       // the wave takes every parts-th group
+    int n_my;        // groups the wave takes
+    int vpage;       // page id of the chunk's page number `lane` (-1: out of range)
+    int slot0;       // LDS row slot of the wave's first row (0..3)
+    int row0;        // the wave's first row
+    int bnd[2];      // exclusive bounds of the wave's rows
+    uint32_t *hist;  // first-digit counters (null: no counting)
+};
+
+// Scores R rows of one wave.  A "unit" is (group, row); units run in order
+// (group 0 row 0, group 0 row 1, group 1 row 0, ...).  In the step of unit u
+// the 16 MFMAs of unit u, the epilogue of unit u-1 and (on a group's last
+// row) the conversion of the next group and the refill of its ring slot are
+// independent, and the scheduler interleaves them: one MFMA, then a few VALU
+// ops.  A group's keys are converted once and used by all R rows.
+template <int R>
+__device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j, float *lds_sc) {
+    const int lane = j.lane;
+    const int kig = lane & 15;      // key of the group this lane loads / scores
+    const int lrow = lane >> 4;     // lane row: 32-byte quarter of the key, 4-head slice of D
+    const uint32_t koff = (uint32_t)(kig * kDim + lrow * 32);
+    const int gc0 = j.c0 / kKeysPerMfma;
+
+    // Loads are unconditional: past the wave's last group they re-read that
+    // group (always in range), so no branch separates a load from its use.
+    // The group's base addresses are wave-uniform; each lane adds its fixed
+    // 32-bit offset.
+    auto load_group = [&](int i, KeyGroup &kg) {
+        const int ic = i < j.n_my ? i : j.n_my - 1;
+        const int g = j.g_first + ic * j.parts;
+        const int page = __builtin_amdgcn_readlane(j.vpage, (g - gc0) >> 2);
+        kg.ok = page >= 0;
+        const int64_t key0 = (int64_t)(kg.ok ? page : 0) * kPage + (g & 3) * kKeysPerMfma;
+        const uint8_t *kbase = a.k8 + key0 * kDim;
+        const float *sbase = a.kscale + key0;
+        kg.lo = *(const u32x4_t *)(kbase + koff);
+        kg.hi = *(const u32x4_t *)(kbase + koff + 16);
+        kg.scale = sbase[kig];
+    };
+
+    // q as the MFMA A operand (head 16*hb + lane%16, dims 32*(lane/16) + 8*ks
+    // + [0, 8)) and the weights of the D rows a lane holds (heads 16*hb +
+    // 4*(lane/16) + jj), issued before the key loads.
+    bf16x8_t qa[R][4][4];
+    f32x4_t wv[R][4];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint16_t *qrow = a.q + (int64_t)(j.row0 + r) * kHeads * kDim;
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                qa[r][hb][ks] = *(const bf16x8_t *)(qrow + (16 * hb + kig) * kDim + 32 * lrow + 8 * ks);
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+            wv[r][hb] = *(const f32x4_t *)(a.w + (int64_t)(j.row0 + r) * kHeads + 16 * hb + 4 * lrow);
+    }
+    KeyGroup kb[kRing];   // group g of the wave lives in slot g % kRing
+#pragma unroll
+    for (int p = 0; p < kRing; ++p) load_group(p, kb[p]);
+    __builtin_amdgcn_sched_barrier(0);   // every load above goes out before any use
+    // q lives in AGPRs: the MFMA reads its A operand from there directly,
+    // leaving the 256 architectural VGPRs to keys, results and weights
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                asm volatile("" : "+a"(qa[r][hb][ks]));
+
+    auto convert = [&](const KeyGroup &kg, bf16x8_t (&kv)[4]) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const u32x4_t &src = ks < 2 ? kg.lo : kg.hi;
+            kv[ks] = e4m3x8_to_bf16(src[(ks & 1) * 2], src[(ks & 1) * 2 + 1]);
+        }
+    };
+    auto scale_of = [&](const KeyGroup &kg) { return kg.ok ? kg.scale : __builtin_nanf(""); };
+    auto mfma_unit = [&](const bf16x8_t (&kv)[4], const bf16x8_t (&q)[4][4], f32x4_t (&acc)[4]) {
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) acc[hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb)
+                acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q[hb][ks], kv[ks], acc[hb], 0, 0, 0);
+    };
+    // lane l holds D[head 16hb + 4(l/16) + jj][key l%16]: weight, ReLU and
+    // sum its 16 heads, then sum the four lane rows
+    auto epilogue = [&](const f32x4_t (&acc)[4], const f32x4_t (&w)[4], float sc) {
+        float part = 0.0f;
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                part = fmaf(w[hb][jj], relu(acc[hb][jj]), part);
+        return lane_sum_64(part) * sc;
+    };
+    // lane row q of out[r] holds row r's score of group g - 3 + q
+    float out[R];
+    auto flush = [&](int g) {
+        const int iq = g - 3 + lrow;
+        const int s = (j.g_first + iq * j.parts) * kKeysPerMfma + kig;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (iq >= 0 && iq < j.n_my && s < j.bnd[r]) {
+                lds_sc[(j.slot0 + r) * j.chunk + (s - j.c0)] = out[r];
+                if (j.hist) {
+                    const uint32_t d = radix_key(out[r]) >> kDigit1Shift;
+                    atomicAdd(j.hist + ((j.slot0 + r) * kBins1 + d) * 64 + ((lane + d) & 63), 1u);
+                }
+            }
+    };
+
+    bf16x8_t kv[2][4];   // converted keys of group g in kv[g & 1]
+    f32x4_t acc[2][4];   // D of unit u in acc[u & 1]
+    float scv[2];        // scale of group g in scv[g & 1]
+#pragma unroll
+    for (int r = 0; r < R; ++r) out[r] = 0.0f;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) acc[1][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    scv[1] = 0.0f;
+    convert(kb[0], kv[0]);
+    scv[0] = scale_of(kb[0]);
+    load_group(kRing, kb[0]);
+
+    const int n_iter = (j.n_my + kRing - 1) / kRing * kRing;
+    for (int i0 = 0; i0 < n_iter; i0 += kRing) {
+#pragma unroll
+        for (int p = 0; p < kRing; ++p) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int u = p * R + r;
+                mfma_unit(kv[p & 1], qa[r], acc[u & 1]);
+                // epilogue of the previous unit: row pr of group i0 + pp
+                // (pp = -1 in the first step: a discarded score)
+                const int pr = (r + R - 1) % R;
+                const int pp = r == 0 ? p - 1 : p;
+                const float score = epilogue(acc[(u + 1) & 1], wv[pr], scv[pp & 1]);
+                if (lrow == (pp & 3)) out[pr] = score;
+                if (r == R - 1) {
+                    KeyGroup &nx = kb[(p + 1) % kRing];
+                    convert(nx, kv[(p + 1) & 1]);
+                    scv[(p + 1) & 1] = scale_of(nx);
+                    load_group(i0 + p + 1 + kRing, nx);
+                }
+#pragma unroll
+                for (int m = 0; m < 16; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // then up to four VALU
+                }
+                if (pr == R - 1 && (pp & 3) == 3) flush(i0 + pp);
+                // nothing moves between steps: the epilogue of a step then
+                // only reads results of MFMAs issued in the step before
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    // epilogue of the last unit (row R-1 of group n_iter - 1; n_iter is a
+    // multiple of 4, so this completes a flush block)
+    {
+        const float score = epilogue(acc[1], wv[R - 1], scv[1]);
+        if (lrow == 3) out[R - 1] = score;
+        flush(n_iter - 1);
+    }
+}
+
 template <bool kHist>
-__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
-    __shared__ uint32_t lds_hist[kGroupRows][kBins1];
-    extern __shared__ float lds_sc[];   // [kGroupRows][chunk] this chunk's scores
+__global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void score_kernel(ScoreArgs a) {
+    // dynamic LDS: [kGroupRows][chunk] f32 scores, then (when counting) the
+    // first-digit counters
+    extern __shared__ __align__(16) float lds_dyn[];
+    float *lds_sc = lds_dyn;
+    uint32_t *lds_cnt = kHist ? (uint32_t *)(lds_dyn + kGroupRows * a.chunk) : nullptr;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r0 = blockIdx.y;
@@ -139,174 +305,80 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     if (c0 >= gmax) return;
     const int c1 = min(c0 + a.chunk, gmax);
 
-    // ---- this wave's row and 16-key groups
-    const int wpr = kGroupRows / rg;                 // waves per row
-    const bool active = wave < rg * wpr;
-    const int slot = wave % rg;
-    const int myrow = r0 + slot;
-    const int wsub = wave / rg;
-    const int b = __builtin_amdgcn_readlane(v_bnd, slot);
-    const int myend = min(c1, b);
-    const int g_first = c0 / kKeysPerMfma + wsub;
+    // ---- wave roles.  4 rows: two row pairs, two waves per pair, each
+    // taking every other 16-key group.  3 rows: a pair and a single row, two
+    // waves each.  2 rows: one pair, 1 row: the row alone; four waves split
+    // the groups four ways.
+    int slot0, nrows, part, parts;
+    if (rg == 4) {
+        slot0 = 2 * (wave & 1); nrows = 2; part = wave >> 1; parts = 2;
+    } else if (rg == 3) {
+        slot0 = wave < 2 ? 0 : 2; nrows = wave < 2 ? 2 : 1; part = wave & 1; parts = 2;
+    } else {
+        slot0 = 0; nrows = rg; part = wave; parts = 4;
+    }
+    WaveJob job;
+    job.lane = lane;
+    job.c0 = c0;
+    job.chunk = a.chunk;
+    job.slot0 = slot0;
+    job.row0 = r0 + slot0;
+    job.bnd[0] = __builtin_amdgcn_readlane(v_bnd, slot0);
+    job.bnd[1] = nrows == 2 ? __builtin_amdgcn_readlane(v_bnd, slot0 + 1) : 0;
+    job.hist = lds_cnt;
+    const int myend = min(c1, max(job.bnd[0], job.bnd[1]));
+    job.g_first = c0 / kKeysPerMfma + part;
+    job.parts = parts;
     const int g_end = (myend + kKeysPerMfma - 1) / kKeysPerMfma;
-    const int n_my = (active && g_first < g_end) ? (g_end - g_first + wpr - 1) / wpr : 0;
-    const bool pt_ok = pr0 >= 0 && pr0 < a.pt_rows;
-    // the chunk's page ids, one per lane (a chunk spans at most 64 pages);
-    // a group picks its page with a lane read, so the loop never waits on a
+    job.n_my = job.g_first < g_end ? (g_end - job.g_first + parts - 1) / parts : 0;
+    // the chunk's page ids, one per lane (a chunk spans at most 64 pages); a
+    // group picks its page with a lane read, so the loop never waits on a
     // scalar load.  Out-of-range ids become -1 (their keys score NaN).
-    int vpage;
     {
+        const bool pt_ok = pr0 >= 0 && pr0 < a.pt_rows;
         const int npg = (c1 - c0 + kPage - 1) / kPage;
         const int32_t *pt = a.page_table + (int64_t)(pt_ok ? pr0 : 0) * a.pt_stride + c0 / kPage;
-        vpage = (pt_ok && lane < npg) ? pt[lane] : -1;
-        vpage = (vpage >= 0 && vpage < a.num_pages) ? vpage : -1;
+        int v = (pt_ok && lane < npg) ? pt[lane] : -1;
+        job.vpage = (v >= 0 && v < a.num_pages) ? v : -1;
     }
 
     if (kHist) {
-        lds_hist[threadIdx.x >> 6][lane] = 0;
+        u32x4_t *c4 = (u32x4_t *)lds_cnt;
+        for (int i = threadIdx.x; i < kHistLds / 4; i += kScoreThreads) c4[i] = u32x4_t{0u, 0u, 0u, 0u};
         __syncthreads();
     }
 
-    const int key_in_group = lane & 15;
-    const int lane_row = lane >> 4;
-    // fixed per-lane byte offsets inside one 16-key group (32 code bytes of
-    // key lane%16) and of its scale; the page and group parts are uniform
-    const uint32_t lane_koff = (uint32_t)(key_in_group * kDim + lane_row * 32);
-    const uint32_t lane_soff = (uint32_t)key_in_group;
-
-    // Loads are unconditional: past the wave's last group they re-read that
-    // group (always in range), so no branch separates a load from its use.
-    // The group's base addresses are wave-uniform (scalar registers); each
-    // lane adds only its fixed 32-bit offset.
-    auto load_group = [&](int i, KeyGroup &kg) {
-        const int ic = i < n_my ? i : n_my - 1;
-        const int g = g_first + ic * wpr;
-        const int page = __builtin_amdgcn_readlane(vpage, (g - c0 / kKeysPerMfma) >> 2);
-        kg.ok = page >= 0;
-        const int64_t key0 = (int64_t)(kg.ok ? page : 0) * kPage + (g & 3) * kKeysPerMfma;
-        const uint8_t *kbase = a.k8 + key0 * kDim;         // uniform
-        const float *sbase = a.kscale + key0;               // uniform
-        kg.lo = *(const u32x4_t *)(kbase + lane_koff);
-        kg.hi = *(const u32x4_t *)(kbase + lane_koff + 16);
-        kg.scale = sbase[lane_soff];
-    };
-
-    if (n_my > 0) {
-    // q as the MFMA A operand: head 16*hb + lane%16, dims 32*(lane/16) + 8*ks + [0, 8),
-    // and the weights of the output rows this lane holds: heads 16*hb + 4*(lane/16) + j.
-    // Issued before the key loads: these do not depend on the page ids.
-    bf16x8_t qa[4][4];
-    f32x4_t wv[4];
-    {
-        const uint16_t *qrow = a.q + (int64_t)myrow * kHeads * kDim;
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                qa[hb][ks] = *(const bf16x8_t *)(qrow + (16 * hb + key_in_group) * kDim + 32 * lane_row + 8 * ks);
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb)
-            wv[hb] = *(const f32x4_t *)(a.w + (int64_t)myrow * kHeads + 16 * hb + 4 * lane_row);
+    if (job.n_my > 0) {
+        if (nrows == 2)
+            score_rows<2>(a, job, lds_sc);
+        else
+            score_rows<1>(a, job, lds_sc);
     }
-    KeyGroup kb[kRing];   // group j lives in slot j % kRing
-#pragma unroll
-    for (int p = 0; p < kRing; ++p) load_group(p, kb[p]);
-    // keep every load above ahead of the first use
-    __builtin_amdgcn_sched_barrier(0);
 
-    float out = 0.0f;
-
-    auto convert = [&](const KeyGroup &kg, bf16x8_t (&kv)[4]) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const u32x4_t &src = ks < 2 ? kg.lo : kg.hi;
-            kv[ks] = e4m3x8_to_bf16(src[(ks & 1) * 2], src[(ks & 1) * 2 + 1]);
-        }
-    };
-    auto scale_of = [&](const KeyGroup &kg) { return kg.ok ? kg.scale : __builtin_nanf(""); };
-    auto mfma_group = [&](const bf16x8_t (&kv)[4], f32x4_t (&acc)[4]) {
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb) acc[hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int hb = 0; hb < 4; ++hb)
-                acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[hb][ks], kv[ks], acc[hb], 0, 0, 0);
-    };
-
-    // Three-stage software pipeline per wave: in the step for group i the
-    // MFMAs of group i+1, the epilogue of group i and the conversion of group
-    // i+2 are independent, and the scheduler interleaves them (one MFMA, then
-    // up to four VALU ops), so the conversion and epilogue run in the MFMA
-    // shadow instead of after it.
-    bf16x8_t kv[2][4];    // group j's converted keys in kv[j & 1]
-    f32x4_t acc[2][4];    // group j's MFMA results in acc[j & 1]
-    float sc0, sc1, sc2;  // scales of groups i, i+1, i+2
-    convert(kb[0], kv[0]);
-    sc0 = scale_of(kb[0]);
-    load_group(kRing, kb[0]);
-    mfma_group(kv[0], acc[0]);
-    convert(kb[1], kv[1]);
-    sc1 = scale_of(kb[1]);
-    load_group(kRing + 1, kb[1]);
-
-    const int n_iter = (n_my + kRing - 1) / kRing * kRing;
-    for (int i0 = 0; i0 < n_iter; i0 += kRing) {
-#pragma unroll
-        for (int p = 0; p < kRing; ++p) {
-            const int i = i0 + p;   // p and i have the same parity (kRing is even)
-            mfma_group(kv[(p + 1) & 1], acc[(p + 1) & 1]);
-            float part = 0.0f;
-#pragma unroll
-            for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    part = fmaf(wv[hb][j], relu(acc[p & 1][hb][j]), part);
-            const float score = lane_sum_64(part) * sc0;
-            if (lane_row == (p & 3)) out = score;
-            KeyGroup &nx = kb[(p + 2) % kRing];
-            convert(nx, kv[p & 1]);
-            sc2 = scale_of(nx);
-            load_group(i + 2 + kRing, nx);
-#pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // then four VALU
-            }
-            if ((p & 3) == 3) {
-                // lane row q holds group i - 3 + q; stage the four groups in
-                // LDS (a global store here would make every later load wait
-                // drain the whole prefetch ring: loads and stores share one
-                // counter and may complete out of order)
-                const int iq = i - 3 + lane_row;
-                const int s = (g_first + iq * wpr) * kKeysPerMfma + key_in_group;
-                if (iq < n_my && s < b) lds_sc[slot * a.chunk + (s - c0)] = out;
-            }
-            sc0 = sc1;
-            sc1 = sc2;
-        }
-    }
-    }  // n_my > 0
-
-    // ---- write the chunk's scores (coalesced) and count their first digit
+    // ---- write the chunk's scores (coalesced, 16 bytes per lane when the
+    // score rows allow it) and add the first-digit counts to the row totals
     __syncthreads();
+    const bool vec4 = (((uintptr_t)a.scores | (uintptr_t)(a.sstride * 4)) & 15) == 0;
     for (int r = 0; r < rg; ++r) {
-        const int n = min(c1, __builtin_amdgcn_readlane(v_bnd, r)) - c0;
+        // keys of this row in the chunk (none when its bound lies before c0)
+        const int n = max(min(c1, __builtin_amdgcn_readlane(v_bnd, r)) - c0, 0);
         float *dst = a.scores + (int64_t)(r0 + r) * a.sstride + c0;
         const float *src = lds_sc + r * a.chunk;
-        for (int j0 = 0; j0 < n; j0 += kScoreThreads) {
-            const int j = j0 + (int)threadIdx.x;
-            const bool v = j < n;
-            const float x = v ? src[j] : 0.0f;
-            if (v) dst[j] = x;
-            if (kHist) count_digit1(lds_hist[r], radix_key(x) >> kDigit1Shift, v, lane);
+        int done = 0;
+        if (vec4) {
+            done = n & ~3;
+            for (int jx = 4 * (int)threadIdx.x; jx < done; jx += 4 * kScoreThreads)
+                *(f32x4_t *)(dst + jx) = *(const f32x4_t *)(src + jx);
         }
+        for (int jx = done + (int)threadIdx.x; jx < n; jx += kScoreThreads) dst[jx] = src[jx];
     }
     if (kHist) {
-        __syncthreads();
-        const int hr = threadIdx.x >> 6;
+        const int hr = threadIdx.x >> 6;   // row slot; lane = digit
         if (hr < rg) {
-            const uint32_t c = lds_hist[hr][lane];
+            const uint32_t *cnt = lds_cnt + (hr * kBins1 + lane) * 64;
+            uint32_t c = 0;
+#pragma unroll 16
+            for (int i = 0; i < 64; ++i) c += cnt[(i + lane) & 63];
             if (c) atomicAdd(a.hist1 + (int64_t)(r0 + hr) * kBins1 + lane, c);
         }
     }
@@ -316,7 +388,7 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t st) {
     if (a.max_bound <= 0) return hipSuccess;
     const int nchunks = (a.max_bound + a.chunk - 1) / a.chunk;
     dim3 grid(nchunks, a.rows);
-    const size_t lds = (size_t)kGroupRows * a.chunk * sizeof(float);
+    const size_t lds = (size_t)kGroupRows * a.chunk * sizeof(float) + (a.hist1 ? kHistLds * sizeof(uint32_t) : 0);
     if (a.hist1)
         hipLaunchKernelGGL(score_kernel<true>, grid, dim3(kScoreThreads), lds, st, a);
     else
