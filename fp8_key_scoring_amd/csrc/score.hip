@@ -79,6 +79,33 @@ __device__ __forceinline__ float lane_sum_64(float v) {
 // bank, and the reduction (lane = digit, summing its 64 counters) does too.
 constexpr int kHistLds = kGroupRows * kBins1 * 64;   // u32 counters
 
+// The same pointer, held in scalar registers and opaque to the optimiser:
+// a load from it plus a 32-bit lane offset then uses the scalar-base
+// addressing form instead of a 64-bit vector add per load.
+template <typename T>
+using gptr = const __attribute__((address_space(1))) T *;   // global memory
+
+template <typename T>
+__device__ __forceinline__ gptr<T> scalar_ptr(const T *p) {
+    uint64_t v = (uint64_t)p;
+    asm volatile("" : "+s"(v));
+    return (gptr<T>)v;
+}
+
+// Sums each of four per-lane partials over the four 16-lane rows and leaves
+// the total of partial q in lane row q (each lane keeps its column): one
+// 32-lane swap round and one 16-lane swap round.
+__device__ __forceinline__ float reduce4(float p0, float p1, float p2, float p3) {
+    const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_int(p0), __float_as_int(p2), false, false);
+    const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_int(p1), __float_as_int(p3), false, false);
+    // lanes 0-31: partial 0 (or 1) summed over lane rows {0,2} / {1,3};
+    // lanes 32-63: the same for partial 2 (or 3)
+    const float a02 = __int_as_float(s02[0]) + __int_as_float(s02[1]);
+    const float a13 = __int_as_float(s13[0]) + __int_as_float(s13[1]);
+    const auto t = __builtin_amdgcn_permlane16_swap(__float_as_int(a02), __float_as_int(a13), false, false);
+    return __int_as_float(t[0]) + __int_as_float(t[1]);
+}
+
 struct KeyGroup {
     u32x4_t lo, hi;   // 32 code bytes of key lane%16
     float scale;
@@ -125,10 +152,10 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
         const int page = __builtin_amdgcn_readlane(j.vpage, (g - gc0) >> 2);
         kg.ok = page >= 0;
         const int64_t key0 = (int64_t)(kg.ok ? page : 0) * kPage + (g & 3) * kKeysPerMfma;
-        const uint8_t *kbase = a.k8 + key0 * kDim;
-        const float *sbase = a.kscale + key0;
-        kg.lo = *(const u32x4_t *)(kbase + koff);
-        kg.hi = *(const u32x4_t *)(kbase + koff + 16);
+        gptr<uint8_t> kbase = scalar_ptr(a.k8 + key0 * kDim);
+        gptr<float> sbase = scalar_ptr(a.kscale + key0);
+        kg.lo = *(gptr<u32x4_t>)(kbase + koff);
+        kg.hi = *(gptr<u32x4_t>)(kbase + koff + 16);
         kg.scale = sbase[kig];
     };
 
@@ -149,6 +176,9 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
         for (int hb = 0; hb < 4; ++hb)
             wv[r][hb] = *(const f32x4_t *)(a.w + (int64_t)(j.row0 + r) * kHeads + 16 * hb + 4 * lrow);
     }
+    // q goes out first: the first MFMA needs it and the first key group, not
+    // the rest of the ring
+    __builtin_amdgcn_sched_barrier(0);
     KeyGroup kb[kRing];   // group g of the wave lives in slot g % kRing
 #pragma unroll
     for (int p = 0; p < kRing; ++p) load_group(p, kb[p]);
@@ -180,43 +210,58 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
             for (int hb = 0; hb < 4; ++hb)
                 acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q[hb][ks], kv[ks], acc[hb], 0, 0, 0);
     };
-    // lane l holds D[head 16hb + 4(l/16) + jj][key l%16]: weight, ReLU and
-    // sum its 16 heads, then sum the four lane rows
-    auto epilogue = [&](const f32x4_t (&acc)[4], const f32x4_t (&w)[4], float sc) {
+    // lane l holds D[head 16hb + 4(l/16) + jj][key l%16]: its weighted,
+    // ReLU'd sum over those 16 heads (the other 48 heads of the key sit in
+    // the other three lane rows)
+    auto partial = [&](const f32x4_t (&acc)[4], const f32x4_t (&w)[4]) {
         float part = 0.0f;
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
                 part = fmaf(w[hb][jj], relu(acc[hb][jj]), part);
-        return lane_sum_64(part) * sc;
+        return part;
     };
-    // lane row q of out[r] holds row r's score of group g - 3 + q
-    float out[R];
-    auto flush = [&](int g) {
+    // Four groups form a block.  P[r][g & 3] is row r's partial of group g;
+    // reduce4 turns a block's four partials into one register whose lane row
+    // q holds the head sum of group 4m + q, which times the scale vector
+    // sv (lane row q: scale of that group's key) is the block's scores.
+    float P[R][4];
+    float sv[2];   // scale vectors of blocks m (sv[m & 1]) being filled / used
+    // g: last group of the block; par: the block's parity (a constant, so
+    // sv stays in registers)
+    auto flush = [&](int g, int par) {
         const int iq = g - 3 + lrow;
         const int s = (j.g_first + iq * j.parts) * kKeysPerMfma + kig;
+        const float scl = sv[par];
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+        for (int r = 0; r < R; ++r) {
+            const float out = reduce4(P[r][0], P[r][1], P[r][2], P[r][3]) * scl;
             if (iq >= 0 && iq < j.n_my && s < j.bnd[r]) {
-                lds_sc[(j.slot0 + r) * j.chunk + (s - j.c0)] = out[r];
+                lds_sc[(j.slot0 + r) * j.chunk + (s - j.c0)] = out;
                 if (j.hist) {
-                    const uint32_t d = radix_key(out[r]) >> kDigit1Shift;
+                    const uint32_t d = radix_key(out) >> kDigit1Shift;
                     atomicAdd(j.hist + ((j.slot0 + r) * kBins1 + d) * 64 + ((lane + d) & 63), 1u);
                 }
             }
+        }
+    };
+    auto take_scale = [&](int g, const KeyGroup &kg) {
+        float &v = sv[(g >> 2) & 1];
+        v = lrow == (g & 3) ? scale_of(kg) : v;
     };
 
     bf16x8_t kv[2][4];   // converted keys of group g in kv[g & 1]
     f32x4_t acc[2][4];   // D of unit u in acc[u & 1]
-    float scv[2];        // scale of group g in scv[g & 1]
 #pragma unroll
-    for (int r = 0; r < R; ++r) out[r] = 0.0f;
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) P[r][q] = 0.0f;
+    sv[0] = sv[1] = 0.0f;
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) acc[1][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    scv[1] = 0.0f;
     convert(kb[0], kv[0]);
-    scv[0] = scale_of(kb[0]);
+    take_scale(0, kb[0]);
     load_group(kRing, kb[0]);
 
     const int n_iter = (j.n_my + kRing - 1) / kRing * kRing;
@@ -227,16 +272,15 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
             for (int r = 0; r < R; ++r) {
                 const int u = p * R + r;
                 mfma_unit(kv[p & 1], qa[r], acc[u & 1]);
-                // epilogue of the previous unit: row pr of group i0 + pp
-                // (pp = -1 in the first step: a discarded score)
+                // partial of the previous unit: row pr of group i0 + pp
+                // (pp = -1 in the first step: a discarded value)
                 const int pr = (r + R - 1) % R;
                 const int pp = r == 0 ? p - 1 : p;
-                const float score = epilogue(acc[(u + 1) & 1], wv[pr], scv[pp & 1]);
-                if (lrow == (pp & 3)) out[pr] = score;
+                P[pr][pp & 3] = partial(acc[(u + 1) & 1], wv[pr]);
                 if (r == R - 1) {
                     KeyGroup &nx = kb[(p + 1) % kRing];
                     convert(nx, kv[(p + 1) & 1]);
-                    scv[(p + 1) & 1] = scale_of(nx);
+                    take_scale(p + 1, nx);
                     load_group(i0 + p + 1 + kRing, nx);
                 }
 #pragma unroll
@@ -244,20 +288,17 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
                     __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // then up to four VALU
                 }
-                if (pr == R - 1 && (pp & 3) == 3) flush(i0 + pp);
-                // nothing moves between steps: the epilogue of a step then
-                // only reads results of MFMAs issued in the step before
+                if (pr == R - 1 && (pp & 3) == 3) flush(i0 + pp, ((pp + 8) >> 2) & 1);
+                // nothing moves between steps: a step only reads results of
+                // MFMAs issued in the step before
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
-    // epilogue of the last unit (row R-1 of group n_iter - 1; n_iter is a
-    // multiple of 4, so this completes a flush block)
-    {
-        const float score = epilogue(acc[1], wv[R - 1], scv[1]);
-        if (lrow == 3) out[R - 1] = score;
-        flush(n_iter - 1);
-    }
+    // partial of the last unit (row R-1 of group n_iter - 1; n_iter is a
+    // multiple of 4, so this completes a block)
+    P[R - 1][3] = partial(acc[1], wv[R - 1]);
+    flush(n_iter - 1, 1);
 }
 
 template <bool kHist>
