@@ -37,6 +37,11 @@ constexpr int kDigit3Shift = kDigit2Shift - kDigit3Bits;     // 10
 constexpr int kBins1 = 1 << kDigit1Bits;                     // 64
 constexpr int kBins2 = 1 << kDigit2Bits;                     // 256
 constexpr int kBins3 = 1 << kDigit3Bits;                     // 256
+// A row's first-digit counts are spread over kHist1Slots copies (workgroup x
+// adds into copy x % kHist1Slots): a row's scores fall into one or two bins,
+// and hundreds of workgroups adding into one word would queue behind each
+// other.  Readers sum the copies.
+constexpr int kHist1Slots = 16;
 
 // Per-row selection state, written by the first gather workgroup of a row.
 struct RowState {
@@ -55,7 +60,7 @@ struct RowState {
 // shapes; the rest of the workspace is scratch that each launch writes before
 // it reads.
 struct WsLayout {
-    size_t hist1;      // u32 [rz][64]      first-digit counts
+    size_t hist1;      // u32 [rz][kHist1Slots][64]  first-digit counts
     size_t hist2;      // u32 [rz][256]     second-digit counts inside the first-digit bin
     size_t hist3;      // u32 [rz][256]     third-digit counts of the candidates
     size_t state;      // RowState [rows]
@@ -85,7 +90,7 @@ inline WsLayout ws_layout(int rows, int max_bound, bool own_scores) {
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
     const size_t rz = (size_t)(rows > kZeroRows ? rows : kZeroRows);
-    L.hist1 = take(rz * kBins1 * 4);
+    L.hist1 = take(rz * kHist1Slots * kBins1 * 4);
     L.hist2 = take(rz * kBins2 * 4);
     L.hist3 = take(rz * kBins3 * 4);
     L.state = take((size_t)rows * sizeof(RowState));

@@ -125,7 +125,6 @@ struct WaveJob {
     int slot0;       // LDS row slot of the wave's first row (0..3)
     int row0;        // the wave's first row
     int bnd[2];      // exclusive bounds of the wave's rows
-    uint32_t *hist;  // first-digit counters (null: no counting)
 };
 
 // Scores R rows of one wave.  A "unit" is (group, row); units run in order
@@ -237,13 +236,7 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const float out = reduce4(P[r][0], P[r][1], P[r][2], P[r][3]) * scl;
-            if (iq >= 0 && iq < j.n_my && s < j.bnd[r]) {
-                lds_sc[(j.slot0 + r) * j.chunk + (s - j.c0)] = out;
-                if (j.hist) {
-                    const uint32_t d = radix_key(out) >> kDigit1Shift;
-                    atomicAdd(j.hist + ((j.slot0 + r) * kBins1 + d) * 64 + ((lane + d) & 63), 1u);
-                }
-            }
+            if (iq >= 0 && iq < j.n_my && s < j.bnd[r]) lds_sc[(j.slot0 + r) * j.chunk + (s - j.c0)] = out;
         }
     };
     auto take_scale = [&](int g, const KeyGroup &kg) {
@@ -366,7 +359,6 @@ void score_kernel(ScoreArgs a) {
     job.row0 = r0 + slot0;
     job.bnd[0] = __builtin_amdgcn_readlane(v_bnd, slot0);
     job.bnd[1] = nrows == 2 ? __builtin_amdgcn_readlane(v_bnd, slot0 + 1) : 0;
-    job.hist = lds_cnt;
     const int myend = min(c1, max(job.bnd[0], job.bnd[1]));
     job.g_first = c0 / kKeysPerMfma + part;
     job.parts = parts;
@@ -405,14 +397,27 @@ void score_kernel(ScoreArgs a) {
         const int n = max(min(c1, __builtin_amdgcn_readlane(v_bnd, r)) - c0, 0);
         float *dst = a.scores + (int64_t)(r0 + r) * a.sstride + c0;
         const float *src = lds_sc + r * a.chunk;
+        uint32_t *cnt = kHist ? lds_cnt + r * kBins1 * 64 : nullptr;
+        auto count = [&](float x) {
+            const uint32_t d = radix_key(x) >> kDigit1Shift;
+            atomicAdd(cnt + d * 64 + ((lane + d) & 63), 1u);
+        };
         int done = 0;
         if (vec4) {
             done = n & ~3;
-            for (int jx = 4 * (int)threadIdx.x; jx < done; jx += 4 * kScoreThreads)
-                *(f32x4_t *)(dst + jx) = *(const f32x4_t *)(src + jx);
+            for (int jx = 4 * (int)threadIdx.x; jx < done; jx += 4 * kScoreThreads) {
+                const f32x4_t x = *(const f32x4_t *)(src + jx);
+                *(f32x4_t *)(dst + jx) = x;
+                if (kHist) { count(x[0]); count(x[1]); count(x[2]); count(x[3]); }
+            }
         }
-        for (int jx = done + (int)threadIdx.x; jx < n; jx += kScoreThreads) dst[jx] = src[jx];
+        for (int jx = done + (int)threadIdx.x; jx < n; jx += kScoreThreads) {
+            const float x = src[jx];
+            dst[jx] = x;
+            if (kHist) count(x);
+        }
     }
+    if (kHist) __syncthreads();
     if (kHist) {
         const int hr = threadIdx.x >> 6;   // row slot; lane = digit
         if (hr < rg) {
@@ -420,7 +425,7 @@ void score_kernel(ScoreArgs a) {
             uint32_t c = 0;
 #pragma unroll 16
             for (int i = 0; i < 64; ++i) c += cnt[(i + lane) & 63];
-            if (c) atomicAdd(a.hist1 + (int64_t)(r0 + hr) * kBins1 + lane, c);
+            if (c) atomicAdd(a.hist1 + ((int64_t)(r0 + hr) * kHist1Slots + blockIdx.x % kHist1Slots) * kBins1 + lane, c);
         }
     }
 }

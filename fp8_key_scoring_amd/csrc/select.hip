@@ -44,6 +44,7 @@ constexpr int kWaves = kSelThreads / 64;
 static_assert(kSelThreads == 1024, "finalize keeps four candidates per thread");
 static_assert(kSelUnroll * kWaves == 128, "gather prefix: two entries per lane");
 static_assert(kCandCap == 4 * kSelThreads, "finalize keeps four candidates per thread");
+static_assert(kHist1Slots * kBins1 <= kSelThreads, "finalize clears the first-digit copies in one pass");
 
 __device__ __forceinline__ uint32_t lane_prefix(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -172,6 +173,15 @@ __device__ __forceinline__ int clamp_bound(int b, int max_bound) {
     return b < 0 ? 0 : (b > max_bound ? max_bound : b);
 }
 
+// Row r's count in first-digit bin `bin`: the sum of its kHist1Slots copies.
+__device__ __forceinline__ uint32_t hist1_total(const SelectArgs &a, int r, int bin) {
+    const uint32_t *h = (const uint32_t *)(a.ws + a.L.hist1) + (int64_t)r * kHist1Slots * kBins1 + bin;
+    uint32_t c = 0;
+#pragma unroll
+    for (int s = 0; s < kHist1Slots; ++s) c += h[s * kBins1];
+    return c;
+}
+
 // ---------------------------------------------------------------- hist1
 // First-digit histogram of stored scores (used when the scores were not
 // produced by this launch's scoring pass).  One LDS copy per wave.
@@ -197,7 +207,7 @@ __global__ __launch_bounds__(kSelThreads) void hist1_kernel(SelectArgs a) {
     if (t < kBins1) {
         uint32_t c = 0;
         for (int w = 0; w < kWaves; ++w) c += h[w][t];
-        if (c) atomicAdd((uint32_t *)(a.ws + a.L.hist1) + (int64_t)r * kBins1 + t, c);
+        if (c) atomicAdd((uint32_t *)(a.ws + a.L.hist1) + ((int64_t)r * kHist1Slots + blockIdx.x % kHist1Slots) * kBins1 + t, c);
     }
 }
 
@@ -219,7 +229,7 @@ __global__ __launch_bounds__(kSelThreads) void refine_kernel(SelectArgs a) {
 
     uint32_t u[kSelUnroll];
     load_keys(row, s0, s1, u);   // the first step's loads overlap the digit search
-    if (t < kBins1) h1[t] = ((const uint32_t *)(a.ws + a.L.hist1))[(int64_t)r * kBins1 + t];
+    if (t < kBins1) h1[t] = hist1_total(a, r, t);
     for (int i = t; i < kWaves * kBins2; i += kSelThreads) (&h2[0][0])[i] = 0;
     if (t == 0) { sb1 = 0; sabove1 = 0; }
     __syncthreads();
@@ -271,7 +281,7 @@ __global__ __launch_bounds__(kSelThreads) void gather_kernel(SelectArgs a) {
     uint32_t u[kSelUnroll];
     if (s0 < s1) load_keys(row, s0, s1, u);   // overlaps the split below
     // ---- the split: (b1, above1) from the first digit, (b2, above2) from the second
-    if (t < kBins1) h1[t] = ((const uint32_t *)(a.ws + a.L.hist1))[(int64_t)r * kBins1 + t];
+    if (t < kBins1) h1[t] = hist1_total(a, r, t);
     if (t < kBins2) {
         h2[t] = ((const uint32_t *)(a.ws + a.L.hist2))[(int64_t)r * kBins2 + t];
         h3[t] = 0;
@@ -541,7 +551,7 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
             out_row[j + lower_bound(su, ns, cj)] = cj;
         }
     }
-    if (t < kBins1) ((uint32_t *)(a.ws + a.L.hist1))[(int64_t)r * kBins1 + t] = 0;
+    if (t < kHist1Slots * kBins1) ((uint32_t *)(a.ws + a.L.hist1))[(int64_t)r * kHist1Slots * kBins1 + t] = 0;
     if (t < kBins2) ((uint32_t *)(a.ws + a.L.hist2))[(int64_t)r * kBins2 + t] = 0;
     if (t < kBins3) hist3[t] = 0;
 }
