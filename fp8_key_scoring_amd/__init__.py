@@ -49,6 +49,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with fp8_key_scoring_amd/build.py "
                           "(or __graft_entry__.build()); there is no fallback path")
+    # torch first: the library then binds to the HIP runtime torch already
+    # loaded, so both see the same devices, streams and allocations
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     lib.fp8idx_abi_version.restype = ctypes.c_int
