@@ -43,7 +43,11 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kRing = 8;   // 16-key groups loaded ahead per wave (a multiple of 4)
+// 16-key groups loaded ahead per wave (a multiple of 4).  A group feeds 16
+// MFMAs per row, so with 3-4 rows four groups ahead cover as much time as
+// eight with 1-2 rows, in half the registers.
+template <int R>
+constexpr int ring_depth() { return R >= 3 ? 4 : 8; }
 
 __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
     bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
@@ -78,6 +82,7 @@ __device__ __forceinline__ float lane_sum_64(float v) {
 // an atomic add collide; with the skew every lane of one add hits its own
 // bank, and the reduction (lane = digit, summing its 64 counters) does too.
 constexpr int kHistLds = kGroupRows * kBins1 * 64;   // u32 counters
+static_assert(kHistLds * 4 == kGroupRows * kHeads * kDim * 2, "the counter region also holds q of four rows");
 
 // The same pointer, held in scalar registers and opaque to the optimiser:
 // a load from it plus a 32-bit lane offset then uses the scalar-base
@@ -112,7 +117,7 @@ struct KeyGroup {
     int ok;           // wave-uniform: the page id was in range
 };
 
-// What one wave scores: R rows (R = 1 or 2) over every parts-th 16-key group
+// What one wave scores: R rows (R = 1..4) over every parts-th 16-key group
 // of the chunk, starting at group g_first.
 struct WaveJob {
     int lane;
@@ -124,7 +129,7 @@ struct WaveJob {
     int vpage;       // page id of the chunk's page number `lane` (-1: out of range)
     int slot0;       // LDS row slot of the wave's first row (0..3)
     int row0;        // the wave's first row
-    int bnd[2];      // exclusive bounds of the wave's rows
+    int bnd[kGroupRows];   // exclusive bounds of the wave's rows
 };
 
 // Scores R rows of one wave.  A "unit" is (group, row); units run in order
@@ -134,7 +139,9 @@ struct WaveJob {
 // independent, and the scheduler interleaves them: one MFMA, then a few VALU
 // ops.  A group's keys are converted once and used by all R rows.
 template <int R>
-__device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j, float *lds_sc) {
+__device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j, float *lds_sc,
+                                           unsigned char *lds_q) {
+    constexpr int kRing = ring_depth<R>();
     const int lane = j.lane;
     const int kig = lane & 15;      // key of the group this lane loads / scores
     const int lrow = lane >> 4;     // lane row: 32-byte quarter of the key, 4-head slice of D
@@ -146,7 +153,7 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
     // The group's base addresses are wave-uniform; each lane adds its fixed
     // 32-bit offset.
     auto load_group = [&](int i, KeyGroup &kg) {
-        const int ic = i < j.n_my ? i : j.n_my - 1;
+        const int ic = max(min(i, j.n_my - 1), 0);   // in range also when n_my == 0
         const int g = j.g_first + ic * j.parts;
         const int page = __builtin_amdgcn_readlane(j.vpage, (g - gc0) >> 2);
         kg.ok = page >= 0;
@@ -158,30 +165,52 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
         kg.scale = sbase[kig];
     };
 
-    // q as the MFMA A operand (head 16*hb + lane%16, dims 32*(lane/16) + 8*ks
-    // + [0, 8)) and the weights of the D rows a lane holds (heads 16*hb +
-    // 4*(lane/16) + jj), issued before the key loads.
+    // q of the group's rows is staged once per workgroup in LDS (every wave
+    // of the workgroup takes part, also one with no groups), the key ring
+    // is issued meanwhile, and each wave then reads q back in MFMA A-operand
+    // order: head 16*hb + lane%16, dims 32*(lane/16) + 8*ks + [0, 8).  In LDS a
+    // head's sixteen 16-byte pieces sit at piece ^ (head % 16), so the sixteen
+    // heads one read instruction touches hit distinct banks.
     bf16x8_t qa[R][4][4];
     f32x4_t wv[R][4];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const uint16_t *qrow = a.q + (int64_t)(j.row0 + r) * kHeads * kDim;
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                qa[r][hb][ks] = *(const bf16x8_t *)(qrow + (16 * hb + kig) * kDim + 32 * lrow + 8 * ks);
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb)
-            wv[r][hb] = *(const f32x4_t *)(a.w + (int64_t)(j.row0 + r) * kHeads + 16 * hb + 4 * lrow);
-    }
-    // q goes out first: the first MFMA needs it and the first key group, not
-    // the rest of the ring
-    __builtin_amdgcn_sched_barrier(0);
     KeyGroup kb[kRing];   // group g of the wave lives in slot g % kRing
+    {
+        constexpr int kPieces = R * kHeads * kDim / 8 / kScoreThreads;   // 16-byte pieces per thread
+        u32x4_t qt[kPieces];
+        const int tid = threadIdx.x;
 #pragma unroll
-    for (int p = 0; p < kRing; ++p) load_group(p, kb[p]);
-    __builtin_amdgcn_sched_barrier(0);   // every load above goes out before any use
+        for (int c = 0; c < kPieces; ++c) {
+            const int ci = tid + c * kScoreThreads;   // piece index: row, head, piece
+            const int r = ci >> 10, h = (ci >> 4) & 63, k = ci & 15;
+            qt[c] = *(gptr<u32x4_t>)(a.q + ((int64_t)(j.row0 + r) * kHeads + h) * kDim + 8 * k);
+        }
+        // weights of the D rows a lane holds: heads 16*hb + 4*(lane/16) + jj
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb)
+                wv[r][hb] = *(gptr<f32x4_t>)(a.w + (int64_t)(j.row0 + r) * kHeads + 16 * hb + 4 * lrow);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int p = 0; p < kRing; ++p) load_group(p, kb[p]);
+        __builtin_amdgcn_sched_barrier(0);   // every load above goes out before any use
+#pragma unroll
+        for (int c = 0; c < kPieces; ++c) {
+            const int ci = tid + c * kScoreThreads;
+            const int r = ci >> 10, h = (ci >> 4) & 63, k = ci & 15;
+            *(u32x4_t *)(lds_q + (((r * kHeads + h) * 16 + (k ^ (h & 15))) * 16)) = qt[c];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    qa[r][hb][ks] = *(const bf16x8_t *)(lds_q + (((r * kHeads + 16 * hb + kig) * 16 +
+                                                                   ((4 * lrow + ks) ^ kig)) * 16));
+    }
+    if (j.n_my == 0) return;
     // q lives in AGPRs: the MFMA reads its A operand from there directly,
     // leaving the 256 architectural VGPRs to keys, results and weights
 #pragma unroll
@@ -226,22 +255,25 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
     // q holds the head sum of group 4m + q, which times the scale vector
     // sv (lane row q: scale of that group's key) is the block's scores.
     float P[R][4];
-    float sv[2];   // scale vectors of blocks m (sv[m & 1]) being filled / used
-    // g: last group of the block; par: the block's parity (a constant, so
-    // sv stays in registers)
-    auto flush = [&](int g, int par) {
+    // scale vectors: sv_fill collects the block being converted, sv_done
+    // holds the last complete block until its flush.  A block is complete
+    // when the first group of the next block is taken, which happens one
+    // step before the flush of the complete block.
+    float sv_fill = 0.0f, sv_done = 0.0f;
+    auto flush = [&](int g) {   // g: last group of the block
         const int iq = g - 3 + lrow;
         const int s = (j.g_first + iq * j.parts) * kKeysPerMfma + kig;
-        const float scl = sv[par];
+        const float scl = sv_done;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const float out = reduce4(P[r][0], P[r][1], P[r][2], P[r][3]) * scl;
             if (iq >= 0 && iq < j.n_my && s < j.bnd[r]) lds_sc[(j.slot0 + r) * j.chunk + (s - j.c0)] = out;
         }
     };
-    auto take_scale = [&](int g, const KeyGroup &kg) {
-        float &v = sv[(g >> 2) & 1];
-        v = lrow == (g & 3) ? scale_of(kg) : v;
+    // q = g & 3 must be a compile-time constant (g = i0 + p, i0 a multiple of 4)
+    auto take_scale = [&](int q, const KeyGroup &kg) {
+        if (q == 0) sv_done = sv_fill;
+        sv_fill = lrow == q ? scale_of(kg) : sv_fill;
     };
 
     bf16x8_t kv[2][4];   // converted keys of group g in kv[g & 1]
@@ -250,11 +282,10 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int q = 0; q < 4; ++q) P[r][q] = 0.0f;
-    sv[0] = sv[1] = 0.0f;
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) acc[1][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     convert(kb[0], kv[0]);
-    take_scale(0, kb[0]);
+    take_scale(0, kb[0]);   // (hands the empty block before group 0 to sv_done)
     load_group(kRing, kb[0]);
 
     const int n_iter = (j.n_my + kRing - 1) / kRing * kRing;
@@ -273,7 +304,7 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
                 if (r == R - 1) {
                     KeyGroup &nx = kb[(p + 1) % kRing];
                     convert(nx, kv[(p + 1) & 1]);
-                    take_scale(p + 1, nx);
+                    take_scale((p + 1) & 3, nx);
                     load_group(i0 + p + 1 + kRing, nx);
                 }
 #pragma unroll
@@ -281,7 +312,7 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
                     __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // then up to four VALU
                 }
-                if (pr == R - 1 && (pp & 3) == 3) flush(i0 + pp, ((pp + 8) >> 2) & 1);
+                if (pr == R - 1 && (pp & 3) == 3) flush(i0 + pp);
                 // nothing moves between steps: a step only reads results of
                 // MFMAs issued in the step before
                 __builtin_amdgcn_sched_barrier(0);
@@ -291,17 +322,17 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
     // partial of the last unit (row R-1 of group n_iter - 1; n_iter is a
     // multiple of 4, so this completes a block)
     P[R - 1][3] = partial(acc[1], wv[R - 1]);
-    flush(n_iter - 1, 1);
+    flush(n_iter - 1);
 }
 
 template <bool kHist>
 __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void score_kernel(ScoreArgs a) {
-    // dynamic LDS: [kGroupRows][chunk] f32 scores, then (when counting) the
-    // first-digit counters
+    // dynamic LDS: [kGroupRows][chunk] f32 scores, then a 64 KB region that
+    // holds q at the start and the first-digit counters at the end
     extern __shared__ __align__(16) float lds_dyn[];
     float *lds_sc = lds_dyn;
-    uint32_t *lds_cnt = kHist ? (uint32_t *)(lds_dyn + kGroupRows * a.chunk) : nullptr;
+    uint32_t *lds_cnt = (uint32_t *)(lds_dyn + kGroupRows * a.chunk);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r0 = blockIdx.y;
@@ -343,23 +374,16 @@ void score_kernel(ScoreArgs a) {
     // taking every other 16-key group.  3 rows: a pair and a single row, two
     // waves each.  2 rows: one pair, 1 row: the row alone; four waves split
     // the groups four ways.
-    int slot0, nrows, part, parts;
-    if (rg == 4) {
-        slot0 = 2 * (wave & 1); nrows = 2; part = wave >> 1; parts = 2;
-    } else if (rg == 3) {
-        slot0 = wave < 2 ? 0 : 2; nrows = wave < 2 ? 2 : 1; part = wave & 1; parts = 2;
-    } else {
-        slot0 = 0; nrows = rg; part = wave; parts = 4;
-    }
+    const int slot0 = 0, nrows = rg, part = wave, parts = 4;
     WaveJob job;
     job.lane = lane;
     job.c0 = c0;
     job.chunk = a.chunk;
     job.slot0 = slot0;
     job.row0 = r0 + slot0;
-    job.bnd[0] = __builtin_amdgcn_readlane(v_bnd, slot0);
-    job.bnd[1] = nrows == 2 ? __builtin_amdgcn_readlane(v_bnd, slot0 + 1) : 0;
-    const int myend = min(c1, max(job.bnd[0], job.bnd[1]));
+#pragma unroll
+    for (int r = 0; r < kGroupRows; ++r) job.bnd[r] = r < nrows ? __builtin_amdgcn_readlane(v_bnd, slot0 + r) : 0;
+    const int myend = min(c1, max(max(job.bnd[0], job.bnd[1]), max(job.bnd[2], job.bnd[3])));
     job.g_first = c0 / kKeysPerMfma + part;
     job.parts = parts;
     const int g_end = (myend + kKeysPerMfma - 1) / kKeysPerMfma;
@@ -375,22 +399,21 @@ void score_kernel(ScoreArgs a) {
         job.vpage = (v >= 0 && v < a.num_pages) ? v : -1;
     }
 
-    if (kHist) {
-        u32x4_t *c4 = (u32x4_t *)lds_cnt;
-        for (int i = threadIdx.x; i < kHistLds / 4; i += kScoreThreads) c4[i] = u32x4_t{0u, 0u, 0u, 0u};
-        __syncthreads();
-    }
-
-    if (job.n_my > 0) {
-        if (nrows == 2)
-            score_rows<2>(a, job, lds_sc);
-        else
-            score_rows<1>(a, job, lds_sc);
+    switch (nrows) {   // every wave, also one with no groups (q staging)
+    case 4: score_rows<4>(a, job, lds_sc, (unsigned char *)lds_cnt); break;
+    case 3: score_rows<3>(a, job, lds_sc, (unsigned char *)lds_cnt); break;
+    case 2: score_rows<2>(a, job, lds_sc, (unsigned char *)lds_cnt); break;
+    default: score_rows<1>(a, job, lds_sc, (unsigned char *)lds_cnt); break;
     }
 
     // ---- write the chunk's scores (coalesced, 16 bytes per lane when the
     // score rows allow it) and add the first-digit counts to the row totals
     __syncthreads();
+    if (kHist) {   // q is no longer needed: the region becomes the counters
+        u32x4_t *c4 = (u32x4_t *)lds_cnt;
+        for (int i = threadIdx.x; i < kHistLds / 4; i += kScoreThreads) c4[i] = u32x4_t{0u, 0u, 0u, 0u};
+        __syncthreads();
+    }
     const bool vec4 = (((uintptr_t)a.scores | (uintptr_t)(a.sstride * 4)) & 15) == 0;
     for (int r = 0; r < rg; ++r) {
         // keys of this row in the chunk (none when its bound lies before c0)
@@ -434,7 +457,7 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t st) {
     if (a.max_bound <= 0) return hipSuccess;
     const int nchunks = (a.max_bound + a.chunk - 1) / a.chunk;
     dim3 grid(nchunks, a.rows);
-    const size_t lds = (size_t)kGroupRows * a.chunk * sizeof(float) + (a.hist1 ? kHistLds * sizeof(uint32_t) : 0);
+    const size_t lds = (size_t)kGroupRows * a.chunk * sizeof(float) + kHistLds * sizeof(uint32_t);
     if (a.hist1)
         hipLaunchKernelGGL(score_kernel<true>, grid, dim3(kScoreThreads), lds, st, a);
     else
