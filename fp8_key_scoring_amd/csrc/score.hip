@@ -38,6 +38,7 @@
 
 namespace fp8idx {
 
+typedef __bf16 bf16_t;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -55,25 +56,6 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
     bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
     bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
     return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-// max(x, 0) in one integer max on the bit pattern: every negative float
-// (sign bit set, -0 included) is a negative int32 and becomes +0; values
-// >= +0 are unchanged.  (A float max would first be canonicalised by the
-// compiler, two instructions per element.)
-__device__ __forceinline__ float relu(float x) {
-    return __int_as_float(max(__float_as_int(x), 0));
-}
-
-__device__ __forceinline__ float lane_sum_64(float v) {
-    // after the 32-swap every lane holds v[l%32] + v[l%32 + 32]; after the
-    // 16-swap every lane holds the sum of its column over all four lane rows
-    int x = __float_as_int(v);
-    auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    float s = __int_as_float(p[0]) + __int_as_float(p[1]);
-    int y = __float_as_int(s);
-    auto q = __builtin_amdgcn_permlane16_swap(y, y, false, false);
-    return __int_as_float(q[0]) + __int_as_float(q[1]);
 }
 
 // First-digit counters in LDS: [row slot][digit][64], one counter per lane
@@ -172,6 +154,7 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
     // head's sixteen 16-byte pieces sit at piece ^ (head % 16), so the sixteen
     // heads one read instruction touches hit distinct banks.
     bf16x8_t qa[R][4][4];
+    bf16x8_t t1a[4];      // A operand of the linear term (below)
     f32x4_t wv[R][4];
     KeyGroup kb[kRing];   // group g of the wave lives in slot g % kRing
     {
@@ -184,12 +167,15 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
             const int r = ci >> 10, h = (ci >> 4) & 63, k = ci & 15;
             qt[c] = *(gptr<u32x4_t>)(a.q + ((int64_t)(j.row0 + r) * kHeads + h) * kDim + 8 * k);
         }
+        // w of this wave's row for the linear term, head = lane
+        const int wave_idx = tid >> 6;
+        const float w_lane = wave_idx < R ? a.w[(int64_t)(j.row0 + wave_idx) * kHeads + lane] : 0.0f;
         // weights of the D rows a lane holds: heads 16*hb + 4*(lane/16) + jj
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int hb = 0; hb < 4; ++hb)
-                wv[r][hb] = *(gptr<f32x4_t>)(a.w + (int64_t)(j.row0 + r) * kHeads + 16 * hb + 4 * lrow);
+                wv[r][hb] = *(gptr<f32x4_t>)(a.w + (int64_t)(j.row0 + r) * kHeads + 16 * hb + 4 * lrow) * 0.5f;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int p = 0; p < kRing; ++p) load_group(p, kb[p]);
@@ -209,6 +195,54 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
                 for (int ks = 0; ks < 4; ++ks)
                     qa[r][hb][ks] = *(const bf16x8_t *)(lds_q + (((r * kHeads + 16 * hb + kig) * 16 +
                                                                    ((4 * lrow + ks) ^ kig)) * 16));
+        // The linear term's A operand: A row 4p + r holds part p of
+        // u_r = (1/2) sum_h w[r][h] q[r][h] (fp32, heads in order), split
+        // into three bf16 parts hi + mid + lo (each residual exact in fp32,
+        // so the three carry u_r to fp32 precision); the other rows are zero.
+        // Wave r computes row r, lane l dims 2l and 2l+1, from q in LDS and
+        // w[r][h] broadcast from lane h.  Written to the score stage, which
+        // is free until the first flush.
+        bf16_t *t1_lds = (bf16_t *)lds_sc;   // [ks][lane][8]
+        if (wave_idx < R) {
+            const int r = wave_idx;
+            const unsigned char *qr = lds_q + r * kHeads * kDim * 2;
+            float u0 = 0.0f, u1 = 0.0f;
+#pragma unroll
+            for (int h0 = 0; h0 < kHeads; h0 += 8) {
+                uint32_t qw[8];
+#pragma unroll
+                for (int h = 0; h < 8; ++h)   // dims 2l, 2l+1 of head h0+h: one 4-byte read
+                    qw[h] = *(const uint32_t *)(qr + ((h0 + h) * 16 + ((lane >> 2) ^ ((h0 + h) & 15))) * 16 +
+                                                (lane & 3) * 4);
+#pragma unroll
+                for (int h = 0; h < 8; ++h) {
+                    const float wh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), h0 + h));
+                    u0 = fmaf(wh, __uint_as_float(qw[h] << 16), u0);
+                    u1 = fmaf(wh, __uint_as_float(qw[h] & 0xffff0000u), u1);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float u = (e ? u1 : u0) * 0.5f;
+                const int d = 2 * lane + e;
+                const bf16_t hi = (bf16_t)u;
+                const float r1 = u - (float)hi;
+                const bf16_t mid = (bf16_t)r1;
+                const bf16_t lo = (bf16_t)(r1 - (float)mid);
+                const int ks = (d & 31) >> 3, lr = d >> 5;
+                t1_lds[(ks * 64 + 0 * 4 + r + 16 * lr) * 8 + (d & 7)] = hi;
+                t1_lds[(ks * 64 + 1 * 4 + r + 16 * lr) * 8 + (d & 7)] = mid;
+                t1_lds[(ks * 64 + 2 * 4 + r + 16 * lr) * 8 + (d & 7)] = lo;
+            }
+        }
+        __syncthreads();
+        const bool t1_row = (kig >> 2) < 3 && (kig & 3) < R;   // this lane's A row is used
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8_t v = *(const bf16x8_t *)(t1_lds + (ks * 64 + lane) * 8);
+            t1a[ks] = t1_row ? v : bf16x8_t{};
+        }
+        __syncthreads();   // the score stage is written from here on
     }
     if (j.n_my == 0) return;
     // q lives in AGPRs: the MFMA reads its A operand from there directly,
@@ -238,17 +272,30 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
             for (int hb = 0; hb < 4; ++hb)
                 acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q[hb][ks], kv[ks], acc[hb], 0, 0, 0);
     };
-    // lane l holds D[head 16hb + 4(l/16) + jj][key l%16]: its weighted,
-    // ReLU'd sum over those 16 heads (the other 48 heads of the key sit in
-    // the other three lane rows)
-    auto partial = [&](const f32x4_t (&acc)[4], const f32x4_t (&w)[4]) {
-        float part = 0.0f;
+    // Epilogue.  sum_h w_h max(d_h, 0) = (1/2) sum_h w_h d_h + sum_h (w_h/2) |d_h|
+    // (max(x, 0) = (x + |x|) / 2).  The first sum is linear in the key,
+    // (1/2) sum_h w_h d_h = u . k with u = (1/2) sum_h w_h q_h, and comes from
+    // one more MFMA block per 16-key group (A rows 4p + r: the bf16 parts of
+    // row r's u; D element r of lane row p is part p's dot product).  The
+    // second is one fma per element with the absolute value as a free source
+    // modifier, instead of a max and an fma.
+    // lane l holds D[head 16hb + 4(l/16) + jj][key l%16]: its sum over those
+    // 16 heads (the other 48 heads of the key sit in the other lane rows),
+    // started from this lane's part of the linear term
+    auto partial = [&](const f32x4_t (&acc)[4], const f32x4_t (&w)[4], float init) {
+        float part = init;
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-                part = fmaf(w[hb][jj], relu(acc[hb][jj]), part);
+                part = fmaf(w[hb][jj], fabsf(acc[hb][jj]), part);
         return part;
+    };
+    auto mfma_linear = [&](const bf16x8_t (&kv)[4], f32x4_t &t) {
+        t = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t1a[ks], kv[ks], t, 0, 0, 0);
     };
     // Four groups form a block.  P[r][g & 3] is row r's partial of group g;
     // reduce4 turns a block's four partials into one register whose lane row
@@ -278,12 +325,14 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
 
     bf16x8_t kv[2][4];   // converted keys of group g in kv[g & 1]
     f32x4_t acc[2][4];   // D of unit u in acc[u & 1]
+    f32x4_t t1[2];       // linear term of group g in t1[g & 1]
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int q = 0; q < 4; ++q) P[r][q] = 0.0f;
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) acc[1][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    t1[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     convert(kb[0], kv[0]);
     take_scale(0, kb[0]);   // (hands the empty block before group 0 to sv_done)
     load_group(kRing, kb[0]);
@@ -296,11 +345,12 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
             for (int r = 0; r < R; ++r) {
                 const int u = p * R + r;
                 mfma_unit(kv[p & 1], qa[r], acc[u & 1]);
+                if (r == 0) mfma_linear(kv[p & 1], t1[p & 1]);
                 // partial of the previous unit: row pr of group i0 + pp
                 // (pp = -1 in the first step: a discarded value)
                 const int pr = (r + R - 1) % R;
                 const int pp = r == 0 ? p - 1 : p;
-                P[pr][pp & 3] = partial(acc[(u + 1) & 1], wv[pr]);
+                P[pr][pp & 3] = partial(acc[(u + 1) & 1], wv[pr], t1[pp & 1][pr]);
                 if (r == R - 1) {
                     KeyGroup &nx = kb[(p + 1) % kRing];
                     convert(nx, kv[(p + 1) & 1]);
@@ -308,7 +358,7 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
                     load_group(i0 + p + 1 + kRing, nx);
                 }
 #pragma unroll
-                for (int m = 0; m < 16; ++m) {
+                for (int m = 0; m < (r == 0 ? 20 : 16); ++m) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
                     __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // then up to four VALU
                 }
@@ -321,7 +371,7 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
     }
     // partial of the last unit (row R-1 of group n_iter - 1; n_iter is a
     // multiple of 4, so this completes a block)
-    P[R - 1][3] = partial(acc[1], wv[R - 1]);
+    P[R - 1][3] = partial(acc[1], wv[R - 1], t1[1][R - 1]);
     flush(n_iter - 1);
 }
 
