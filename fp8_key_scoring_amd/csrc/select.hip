@@ -159,16 +159,6 @@ __device__ __forceinline__ int lower_bound(const int32_t *a, int n, int32_t v) {
     return lo;
 }
 
-// Last slice x in [0, n) whose offset off[x] is <= p.
-__device__ __forceinline__ int slice_of(const uint32_t *off, int n, uint32_t p) {
-    int lo = 0, hi = n - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= p) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-
 __device__ __forceinline__ int clamp_bound(int b, int max_bound) {
     return b < 0 ? 0 : (b > max_bound ? max_bound : b);
 }
@@ -426,6 +416,7 @@ __device__ void fallback_select(const float *row, int b, uint32_t T14, uint32_t 
 // row's histograms zeroed.
 __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
     __shared__ unsigned long long tie[kTieCap];   // candidates inside the third-digit bin
+    __shared__ unsigned long long cand[kCandCap]; // all candidates (key << 32 | index), ascending index
     __shared__ int32_t su[kMaxTopk];              // sure keys, ascending
     __shared__ int32_t chs[kMaxTopk];             // chosen candidates, ascending
     __shared__ uint32_t offs[kSelMaxWgs + 1], offc[kSelMaxWgs + 1];
@@ -469,23 +460,32 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
         const int ns = (int)min(offs[kSelMaxWgs], (uint32_t)(k - need));
         const int nc = (int)offc[kSelMaxWgs];
         bool overflow = ovf != 0u;
-        // the sure keys: slices concatenated in workgroup order are ascending
+        // The slices' lists, concatenated in workgroup order (ascending key
+        // index), are copied to LDS: 16 threads per slice, each taking every
+        // 16th entry, so every load address is known without a search.
         {
-            int32_t v0 = 0, v1 = 0;
-            const int p0 = t, p1 = t + kSelThreads;
-            if (p0 < ns) { const int xs = slice_of(offs, S, p0); v0 = sl_s[(int64_t)xs * kMaxTopk + (p0 - (int)offs[xs])]; }
-            if (p1 < ns) { const int xs = slice_of(offs, S, p1); v1 = sl_s[(int64_t)xs * kMaxTopk + (p1 - (int)offs[xs])]; }
-            if (p0 < ns) su[p0] = v0;
-            if (p1 < ns) su[p1] = v1;
+            const int x = t >> 4, j0 = t & 15;
+            if (x < S) {
+                const int nsx = (int)min(scnt[x], (uint32_t)kMaxTopk);
+                const int o = (int)offs[x];
+                for (int jj = j0; jj < nsx; jj += 16)
+                    if (o + jj < ns) su[o + jj] = sl_s[(int64_t)x * kMaxTopk + jj];
+                if (!overflow) {
+                    const int ncx = (int)ccnt[x];
+                    const int oc = (int)offc[x];
+                    for (int jj = j0; jj < ncx; jj += 16)
+                        cand[oc + jj] = sl_c[(int64_t)x * kCandSlice + jj];
+                }
+            }
         }
+        __syncthreads();
         unsigned long long c[4];
         if (!overflow) {
             // this thread's candidates t*4 .. t*4+3 (ascending index)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int i = t * 4 + q;
-                c[q] = 0ull;
-                if (i < nc) { const int xc = slice_of(offc, S, i); c[q] = sl_c[(int64_t)xc * kCandSlice + (i - (int)offc[xc])]; }
+                c[q] = i < nc ? cand[i] : 0ull;
             }
             if (t < 64) wave_find_bin(h3, kBins3 / 64, (uint32_t)need, lane, &sB, &sAbove);
             __syncthreads();
