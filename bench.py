@@ -124,6 +124,59 @@ def copy_calib():
     print(json.dumps({"copy_calib_bytes_read_per_copy": n, "copies": 5}))
 
 
+def measured_peaks(torch, dev):
+    """Sustained HBM read rate and dense bf16 MFMA rate of this device, from
+    the two measurement kernels in libfp8idx_peaks.so (16-byte streaming
+    loads over 4 GiB; v_mfma_f32_16x16x32_bf16 with eight independent
+    accumulators and random operands), each the best over a few grid sizes."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "fp8_key_scoring_amd", "libfp8idx_peaks.so"))
+    lib.peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.peak_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(3)
+    sink = torch.zeros(16384, dtype=torch.int32, device=dev)
+
+    def rd(blocks):
+        if lib.peak_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                         blocks, sp):
+            raise RuntimeError("peak_read launch failed")
+    # best over a few grid sizes (the rate a well-shaped kernel can reach)
+    read_s = min(timed(lambda: rd(b), 10) for b in (2048, 4096, 8192, 16384))
+    del buf
+    g = torch.Generator().manual_seed(11)
+    opnd = torch.randn(64 * 6 * 8, generator=g).to(torch.bfloat16).to(dev)
+    iters = 2048
+    outm = torch.zeros(1024, dtype=torch.float32, device=dev)
+
+    def mm(blocks):
+        if lib.peak_mfma(ctypes.c_void_p(opnd.data_ptr()), ctypes.c_void_p(outm.data_ptr()), iters,
+                         blocks, sp):
+            raise RuntimeError("peak_mfma launch failed")
+    mfma_tf = max(b * 4 * iters * 16 * (2 * 16 * 16 * 32) / timed(lambda: mm(b), 5) / 1e12
+                  for b in (256, 512, 1024))
+    return {"hbm_read_GBs": round(nbytes / read_s / 1e9, 1),
+            "bf16_mfma_TFLOPs": round(mfma_tf, 1),
+            "how": "best over grid sizes of: streaming 16-byte loads over 4 GiB; "
+                   "v_mfma_f32_16x16x32_bf16 with 8 accumulators, 1-4 waves/SIMD, random operands"}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -210,6 +263,10 @@ def main():
                  "kernel_us": round(score_ms * 1e3, 2), "traffic_unit": "bytes per launch",
                  "algorithmic_flops": flops, "algorithmic_bytes": abytes,
                  "hbm_gbs_at_kernel_time": round(ach_gbs, 1)})
+    peaks = measured_peaks(torch, dev)
+    mpeak = peaks["bf16_mfma_TFLOPs"] if mfma_bound else peaks["hbm_read_GBs"]
+    roof.update({"measured_peak": mpeak, "frac_of_measured_peak": round(roof["achieved"] / mpeak, 4),
+                 "measured_peaks": peaks})
     step_roof_s = max(flops / (PEAK_BF16_TFLOPS * 1e12), abytes / (PEAK_HBM_GBS * 1e9))
 
     res = {

@@ -9,6 +9,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfp8idx.so")
+# measurement helpers for bench.py (peak HBM read and MFMA rates); not the indexer
+PEAKS_LIB = os.path.join(HERE, "libfp8idx_peaks.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -39,7 +41,20 @@ def build(verbose: bool = False) -> str:
     if verbose and msgs:
         print("\n".join(msgs))
     os.replace(tmp, LIB)
+    _build_peaks(verbose)
     return LIB
+
+
+def _build_peaks(verbose: bool) -> None:
+    tmp = PEAKS_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, os.path.join(HERE, "peaks", "peaks.hip"), "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = [l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l and l.strip()]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, PEAKS_LIB)
 
 
 if __name__ == "__main__":

@@ -1,0 +1,67 @@
+// Measurement helpers for the benchmark, not part of the indexer: the
+// device's sustained HBM read rate and bf16 MFMA rate, measured with the
+// instruction forms the indexer itself uses (16-byte global loads and
+// v_mfma_f32_16x16x32_bf16), so the kernel's roofline fraction can be stated
+// against both the published and the measured peak.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Streaming read: grid-stride 16-byte loads, four in flight per thread,
+// folded with xor; a word is stored only if the fold hits a sentinel, which
+// keeps the loads alive without a store per thread.
+__global__ __launch_bounds__(256) void read_kernel(const u32x4_t *src, size_t n16, uint32_t *out) {
+    u32x4_t acc = {0u, 0u, 0u, 0u};
+    const size_t stride = (size_t)gridDim.x * 256;
+    size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4_t v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
+        acc ^= v0 ^ v1 ^ v2 ^ v3;
+    }
+    for (; i < n16; i += stride) acc ^= src[i];
+    const uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    if (x == 0x9E3779B9u) out[blockIdx.x] = x;
+}
+
+// MFMA loop: eight independent accumulators per wave, two waves per SIMD.
+__global__ __launch_bounds__(256) void mfma_kernel(const bf16x8_t *in, float *out, int iters) {
+    const int lane = threadIdx.x & 63;
+    bf16x8_t a[4], b[2];
+    for (int i = 0; i < 4; ++i) a[i] = in[lane * 6 + i];
+    for (int i = 0; i < 2; ++i) b[i] = in[lane * 6 + 4 + i];
+    f32x4_t acc[8];
+    for (int i = 0; i < 8; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+            acc[m & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m & 3], b[(m >> 2) & 1], acc[m & 7], 0, 0, 0);
+    }
+    float s = 0.f;
+    for (int i = 0; i < 8; ++i) s += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+    if (s == 1234.5f) out[blockIdx.x] = s;
+}
+
+extern "C" {
+
+// Reads `bytes` (a multiple of 16) from device memory at `src` once.
+int peak_read(const void *src, size_t bytes, uint32_t *out, int blocks, void *stream) {
+    if (!src || !out || bytes % 16 || blocks < 1) return -1;
+    hipLaunchKernelGGL(read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       (const u32x4_t *)src, bytes / 16, out);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+// `blocks` workgroups of 4 waves, each wave `iters` x 16 MFMAs.  `in` holds
+// 64 * 6 bf16x8 operands (3 KB).
+int peak_mfma(const void *in, float *out, int iters, int blocks, void *stream) {
+    if (!in || !out || iters < 1 || blocks < 1) return -1;
+    hipLaunchKernelGGL(mfma_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       (const bf16x8_t *)in, out, iters);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+}  // extern "C"
