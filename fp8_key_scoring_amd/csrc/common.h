@@ -14,7 +14,8 @@ constexpr int kPage = 64;
 constexpr int kMaxTopk = 2048;
 
 // Scoring: one workgroup = 4 waves; up to 4 rows that share a page-table row
-// are scored together (one wave per row, each key read from HBM once).
+// are scored together (each wave scores all of them on every fourth 16-key
+// group, so each key is read from HBM once and converted once).
 constexpr int kScoreThreads = 256;
 constexpr int kGroupRows = 4;
 constexpr int kKeysPerMfma = 16;   // one 16x16x32 MFMA column block = 16 keys
@@ -43,14 +44,16 @@ constexpr int kBins3 = 1 << kDigit3Bits;                     // 256
 // other.  Readers sum the copies.
 constexpr int kHist1Slots = 16;
 
-// Per-row selection state, written by the first gather workgroup of a row.
+// Per-row selection state: b1 and above1 written by the first refine
+// workgroup of a row, the rest by the first gather workgroup.
 struct RowState {
     uint32_t b1;      // first-digit bin holding the k-th largest key
     uint32_t b2;      // second-digit bin inside b1 holding it
     uint32_t sure;    // keys whose top 14 bits exceed (b1, b2): all selected
     uint32_t need;    // keys still to take from the (b1, b2) bin
     uint32_t cand;    // keys in the (b1, b2) bin
-    uint32_t pad[3];
+    uint32_t above1;  // keys in first-digit bins above b1 (written with b1 by refine)
+    uint32_t pad[2];
 };
 
 // Workspace layout.  The histograms must be zero before a launch; every

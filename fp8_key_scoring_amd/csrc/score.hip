@@ -64,6 +64,7 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
 // an atomic add collide; with the skew every lane of one add hits its own
 // bank, and the reduction (lane = digit, summing its 64 counters) does too.
 constexpr int kHistLds = kGroupRows * kBins1 * 64;   // u32 counters
+constexpr int kBlockPieces = kGroupRows * kHeads * kDim / 8 / kScoreThreads;   // q pieces per thread, 4 rows
 static_assert(kHistLds * 4 == kGroupRows * kHeads * kDim * 2, "the counter region also holds q of four rows");
 
 // The same pointer, held in scalar registers and opaque to the optimiser:
@@ -93,6 +94,32 @@ __device__ __forceinline__ float reduce4(float p0, float p1, float p2, float p3)
     return __int_as_float(t[0]) + __int_as_float(t[1]);
 }
 
+// q in LDS: [row slot][head][16 pieces of 16 bytes], piece p of head h at
+// position p ^ (h % 16), so the sixteen heads that one A-operand read
+// instruction touches hit distinct banks.
+__device__ __forceinline__ int q_lds_off(int r, int h, int piece) {
+    return ((r * kHeads + h) * 16 + (piece ^ (h & 15))) * 16;
+}
+
+// Loads q of rows row0 .. row0+R-1 (every thread of the workgroup a share)
+// and writes it to LDS row slots 0..R-1.
+template <int R>
+__device__ __forceinline__ void stage_q(const ScoreArgs &a, int row0, int tid, unsigned char *lds_q) {
+    constexpr int kPieces = R * kHeads * kDim / 8 / kScoreThreads;   // 16-byte pieces per thread
+    u32x4_t qt[kPieces];
+#pragma unroll
+    for (int c = 0; c < kPieces; ++c) {
+        const int ci = tid + c * kScoreThreads;   // piece index: row, head, piece
+        qt[c] = *(gptr<u32x4_t>)(a.q + ((int64_t)(row0 + (ci >> 10)) * kHeads + ((ci >> 4) & 63)) * kDim +
+                                 8 * (ci & 15));
+    }
+#pragma unroll
+    for (int c = 0; c < kPieces; ++c) {
+        const int ci = tid + c * kScoreThreads;
+        *(u32x4_t *)(lds_q + q_lds_off(ci >> 10, (ci >> 4) & 63, ci & 15)) = qt[c];
+    }
+}
+
 struct KeyGroup {
     u32x4_t lo, hi;   // 32 code bytes of key lane%16
     float scale;
@@ -102,6 +129,7 @@ struct KeyGroup {
 // What one wave scores: R rows (R = 1..4) over every parts-th 16-key group
 // of the chunk, starting at group g_first.
 struct WaveJob {
+    int tid;         // thread index in the workgroup
     int lane;
     int c0;          // first key of the chunk (a multiple of 64)
     int chunk;       // keys per chunk (row stride of the LDS score buffer)
@@ -122,7 +150,7 @@ struct WaveJob {
 // ops.  A group's keys are converted once and used by all R rows.
 template <int R>
 __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j, float *lds_sc,
-                                           unsigned char *lds_q) {
+                                           unsigned char *lds_q, int q_slot, bool staged, float w_blk) {
     constexpr int kRing = ring_depth<R>();
     const int lane = j.lane;
     const int kig = lane & 15;      // key of the group this lane loads / scores
@@ -147,73 +175,58 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
         kg.scale = sbase[kig];
     };
 
-    // q of the group's rows is staged once per workgroup in LDS (every wave
-    // of the workgroup takes part, also one with no groups), the key ring
-    // is issued meanwhile, and each wave then reads q back in MFMA A-operand
-    // order: head 16*hb + lane%16, dims 32*(lane/16) + 8*ks + [0, 8).  In LDS a
-    // head's sixteen 16-byte pieces sit at piece ^ (head % 16), so the sixteen
-    // heads one read instruction touches hit distinct banks.
+    // q of the group's rows sits in LDS, one 16 KB row after another from
+    // row slot q_slot: staged with the workgroup's block of rows, or here
+    // when the group's rows were not.  Each wave reads q back in MFMA
+    // A-operand order (head 16*hb + lane%16, dims 32*(lane/16) + 8*ks +
+    // [0, 8)) straight into the registers the MFMAs read.  The order of the
+    // set-up favours the key stream: q reads go out first, the key ring as
+    // soon as the page ids are in, the linear term (LDS and VALU work) last.
     bf16x8_t qa[R][4][4];
     bf16x8_t t1a[4];      // A operand of the linear term (below)
     f32x4_t wv[R][4];
     KeyGroup kb[kRing];   // group g of the wave lives in slot g % kRing
     {
-        constexpr int kPieces = R * kHeads * kDim / 8 / kScoreThreads;   // 16-byte pieces per thread
-        u32x4_t qt[kPieces];
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int c = 0; c < kPieces; ++c) {
-            const int ci = tid + c * kScoreThreads;   // piece index: row, head, piece
-            const int r = ci >> 10, h = (ci >> 4) & 63, k = ci & 15;
-            qt[c] = *(gptr<u32x4_t>)(a.q + ((int64_t)(j.row0 + r) * kHeads + h) * kDim + 8 * k);
-        }
-        // w of this wave's row for the linear term, head = lane
+        const int tid = j.tid;
         const int wave_idx = tid >> 6;
-        const float w_lane = wave_idx < R ? a.w[(int64_t)(j.row0 + wave_idx) * kHeads + lane] : 0.0f;
-        // weights of the D rows a lane holds: heads 16*hb + 4*(lane/16) + jj
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int hb = 0; hb < 4; ++hb)
-                wv[r][hb] = *(gptr<f32x4_t>)(a.w + (int64_t)(j.row0 + r) * kHeads + 16 * hb + 4 * lrow) * 0.5f;
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int p = 0; p < kRing; ++p) load_group(p, kb[p]);
-        __builtin_amdgcn_sched_barrier(0);   // every load above goes out before any use
-#pragma unroll
-        for (int c = 0; c < kPieces; ++c) {
-            const int ci = tid + c * kScoreThreads;
-            const int r = ci >> 10, h = (ci >> 4) & 63, k = ci & 15;
-            *(u32x4_t *)(lds_q + (((r * kHeads + h) * 16 + (k ^ (h & 15))) * 16)) = qt[c];
+        if (!staged) {   // q_slot is 0 here
+            stage_q<R>(a, j.row0, tid, lds_q);
+            __syncthreads();
         }
-        __syncthreads();
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
-                    qa[r][hb][ks] = *(const bf16x8_t *)(lds_q + (((r * kHeads + 16 * hb + kig) * 16 +
-                                                                   ((4 * lrow + ks) ^ kig)) * 16));
+                    qa[r][hb][ks] = *(const bf16x8_t *)(lds_q + q_lds_off(q_slot + r, 16 * hb + kig, 4 * lrow + ks));
+        // weights of the D rows a lane holds: heads 16*hb + 4*(lane/16) + jj
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb)
+                wv[r][hb] = *(gptr<f32x4_t>)(a.w + (int64_t)(j.row0 + r) * kHeads + 16 * hb + 4 * lrow) * 0.5f;
+#pragma unroll
+        for (int p = 0; p < kRing; ++p) load_group(p, kb[p]);
         // The linear term's A operand: A row 4p + r holds part p of
         // u_r = (1/2) sum_h w[r][h] q[r][h] (fp32, heads in order), split
         // into three bf16 parts hi + mid + lo (each residual exact in fp32,
         // so the three carry u_r to fp32 precision); the other rows are zero.
-        // Wave r computes row r, lane l dims 2l and 2l+1, from q in LDS and
-        // w[r][h] broadcast from lane h.  Written to the score stage, which
-        // is free until the first flush.
+        // Wave q_slot + r computes row r, lane l dims 2l and 2l+1, from q in
+        // LDS and w[r][h] broadcast from lane h.  Written to the score stage,
+        // which is free until the first flush.
         bf16_t *t1_lds = (bf16_t *)lds_sc;   // [ks][lane][8]
-        if (wave_idx < R) {
-            const int r = wave_idx;
-            const unsigned char *qr = lds_q + r * kHeads * kDim * 2;
+        const int ur = wave_idx - q_slot;
+        if (ur >= 0 && ur < R) {
+            const float w_lane = staged ? w_blk : a.w[(int64_t)(j.row0 + ur) * kHeads + lane];
+            const unsigned char *qr = lds_q + q_lds_off(q_slot + ur, 0, 0);
             float u0 = 0.0f, u1 = 0.0f;
 #pragma unroll
             for (int h0 = 0; h0 < kHeads; h0 += 8) {
                 uint32_t qw[8];
 #pragma unroll
                 for (int h = 0; h < 8; ++h)   // dims 2l, 2l+1 of head h0+h: one 4-byte read
-                    qw[h] = *(const uint32_t *)(qr + ((h0 + h) * 16 + ((lane >> 2) ^ ((h0 + h) & 15))) * 16 +
-                                                (lane & 3) * 4);
+                    qw[h] = *(const uint32_t *)(qr + q_lds_off(0, h0 + h, lane >> 2) + (lane & 3) * 4);
 #pragma unroll
                 for (int h = 0; h < 8; ++h) {
                     const float wh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), h0 + h));
@@ -230,9 +243,9 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
                 const bf16_t mid = (bf16_t)r1;
                 const bf16_t lo = (bf16_t)(r1 - (float)mid);
                 const int ks = (d & 31) >> 3, lr = d >> 5;
-                t1_lds[(ks * 64 + 0 * 4 + r + 16 * lr) * 8 + (d & 7)] = hi;
-                t1_lds[(ks * 64 + 1 * 4 + r + 16 * lr) * 8 + (d & 7)] = mid;
-                t1_lds[(ks * 64 + 2 * 4 + r + 16 * lr) * 8 + (d & 7)] = lo;
+                t1_lds[(ks * 64 + 0 * 4 + ur + 16 * lr) * 8 + (d & 7)] = hi;
+                t1_lds[(ks * 64 + 1 * 4 + ur + 16 * lr) * 8 + (d & 7)] = mid;
+                t1_lds[(ks * 64 + 2 * 4 + ur + 16 * lr) * 8 + (d & 7)] = lo;
             }
         }
         __syncthreads();
@@ -385,120 +398,188 @@ void score_kernel(ScoreArgs a) {
     uint32_t *lds_cnt = (uint32_t *)(lds_dyn + kGroupRows * a.chunk);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int r0 = blockIdx.y;
+    const int yb = blockIdx.y * kGroupRows;   // first row of this block of rows
 
-    // ---- row grouping: rows sharing a page-table row, in runs of up to 4.
-    // One round of loads: every lane reads one of the 64 rows before r0 (to
-    // find where r0's run of equal page-table rows starts), and lanes 0..3
-    // read the page-table rows and bounds of r0..r0+3.
-    const int back = r0 - 1 - lane;
-    const int fwd = r0 + (lane & 3);
-    const int v_back = back >= 0 ? a.row_pt[back] : 0;
-    const int v_fwd = fwd < a.rows ? a.row_pt[fwd] : 0;
-    int v_bnd = fwd < a.rows ? a.row_bound[fwd] : 0;
+    // ---- row groups: up to 4 consecutive rows sharing a page-table row (a
+    // run of equal page-table rows is cut into groups from its start).  This
+    // workgroup scores the groups whose first row lies in its block of 4
+    // rows: one group when requests' rows come in aligned fours, up to four.
+    // One round of loads: lane l reads the page-table row of row yb+3-l (run
+    // starts), lanes 0..6 the page-table rows and bounds of rows yb..yb+6
+    // (group extents).
+    const int back = yb + kGroupRows - 1 - lane;
+    const int fwd = yb + lane;
+    const bool fwd_ok = lane < 2 * kGroupRows - 1 && fwd < a.rows;
+    const int v_back = (back >= 0 && back < a.rows) ? a.row_pt[back] : 0;
+    const int v_fwd = fwd_ok ? a.row_pt[fwd] : 0;
+    int v_bnd = fwd_ok ? a.row_bound[fwd] : 0;
+    // q and w of the block's rows depend on nothing else: their loads go out
+    // right behind the planning loads (q reaches LDS once the first group is
+    // known to lie in the block).  Loads complete in order, so the planning
+    // loads must be issued first for the planning to wait on them alone.
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4_t qt_blk[kBlockPieces];
+#pragma unroll
+    for (int c = 0; c < kBlockPieces; ++c) {
+        const int ci = threadIdx.x + c * kScoreThreads;   // piece index: row, head, piece
+        const int row = min(yb + (ci >> 10), a.rows - 1);   // rows past the end: never used
+        qt_blk[c] = *(gptr<u32x4_t>)(a.q + ((int64_t)row * kHeads + ((ci >> 4) & 63)) * kDim + 8 * (ci & 15));
+    }
+    const float w_blk = a.w[(int64_t)min(yb + wave, a.rows - 1) * kHeads + lane];
+    __builtin_amdgcn_sched_barrier(0);
     v_bnd = v_bnd < 0 ? 0 : (v_bnd > a.max_bound ? a.max_bound : v_bnd);
-    const int pr0 = __builtin_amdgcn_readlane(v_fwd, 0);
-    int rs;
-    {
-        const uint64_t m = __ballot(back < 0 || v_back != pr0);
-        if (m) {
-            rs = r0 - (__ffsll((unsigned long long)m) - 1);
-        } else {   // the run is longer than 64 rows: keep walking back
-            rs = 0;
-            for (int base = r0 - 64; base > 0; base -= 64) {
-                const int idx = base - 1 - lane;
-                const uint64_t m2 = __ballot(idx < 0 || a.row_pt[idx < 0 ? 0 : idx] != pr0);
-                if (m2) { rs = base - (__ffsll((unsigned long long)m2) - 1); break; }
-            }
+    // row `back` starts a run when it is row 0 or differs from row back-1
+    // (lane 63 does not see its predecessor and never claims a start)
+    const int v_prev = __shfl_down(v_back, 1);
+    const uint64_t starts =
+        __ballot(back == 0 || (back > 0 && back < a.rows && lane < 63 && v_prev != v_back));
+    // No run start among rows yb-59 .. yb: row yb's run reaches back past
+    // row yb-60 (lane 63), so walk back 64 rows per round.  Only block rows
+    // whose window holds no start take this value.
+    int rs_far = 0;
+    if ((starts >> (kGroupRows - 1)) == 0) {
+        const int pr_far = __builtin_amdgcn_readlane(v_back, kGroupRows - 1);   // row yb
+        for (int base = yb - 60; base > 0; base -= 64) {
+            const int idx = base - 1 - lane;
+            const uint64_t m2 = __ballot(idx < 0 || a.row_pt[idx < 0 ? 0 : idx] != pr_far);
+            if (m2) { rs_far = base - (__ffsll((unsigned long long)m2) - 1); break; }
         }
     }
-    if ((r0 - rs) % kGroupRows != 0) return;
-    const int rg = __ffsll((unsigned long long)~__ballot(lane < kGroupRows && fwd < a.rows && v_fwd == pr0)) - 1;
-    int gmax = 0;
-    for (int j = 0; j < rg; ++j) gmax = max(gmax, __builtin_amdgcn_readlane(v_bnd, j));
+    // The group led by block row bi, if any, with its row count and the
+    // largest bound among its rows.
     const int c0 = blockIdx.x * a.chunk;
-    if (c0 >= gmax) return;
-    const int c1 = min(c0 + a.chunk, gmax);
-
-    // ---- wave roles.  4 rows: two row pairs, two waves per pair, each
-    // taking every other 16-key group.  3 rows: a pair and a single row, two
-    // waves each.  2 rows: one pair, 1 row: the row alone; four waves split
-    // the groups four ways.
-    const int slot0 = 0, nrows = rg, part = wave, parts = 4;
-    WaveJob job;
-    job.lane = lane;
-    job.c0 = c0;
-    job.chunk = a.chunk;
-    job.slot0 = slot0;
-    job.row0 = r0 + slot0;
-#pragma unroll
-    for (int r = 0; r < kGroupRows; ++r) job.bnd[r] = r < nrows ? __builtin_amdgcn_readlane(v_bnd, slot0 + r) : 0;
-    const int myend = min(c1, max(max(job.bnd[0], job.bnd[1]), max(job.bnd[2], job.bnd[3])));
-    job.g_first = c0 / kKeysPerMfma + part;
-    job.parts = parts;
-    const int g_end = (myend + kKeysPerMfma - 1) / kKeysPerMfma;
-    job.n_my = job.g_first < g_end ? (g_end - job.g_first + parts - 1) / parts : 0;
-    // the chunk's page ids, one per lane (a chunk spans at most 64 pages); a
-    // group picks its page with a lane read, so the loop never waits on a
-    // scalar load.  Out-of-range ids become -1 (their keys score NaN).
-    {
+    auto group_at = [&](int bi, int &rg, int &gmax) {
+        const int r0 = yb + bi;
+        if (r0 >= a.rows) return false;
+        const uint64_t m = starts >> (kGroupRows - 1 - bi);
+        const int rs = m ? r0 - (__ffsll((unsigned long long)m) - 1) : rs_far;
+        if ((r0 - rs) % kGroupRows != 0) return false;   // not the first row of a group
+        const int pr0 = __builtin_amdgcn_readlane(v_fwd, bi);
+        const uint64_t same = __ballot(fwd_ok && v_fwd == pr0) >> bi;
+        rg = min(__ffsll((unsigned long long)~same) - 1, kGroupRows);
+        gmax = 0;
+        for (int j = 0; j < rg; ++j) gmax = max(gmax, __builtin_amdgcn_readlane(v_bnd, bi + j));
+        return c0 < gmax;
+    };
+    // the chunk's page ids of a group, one per lane (a chunk spans at most 64
+    // pages); a 16-key group picks its page with a lane read, so the loop
+    // never waits on a scalar load.  Out-of-range ids become -1 (their keys
+    // score NaN).
+    auto load_pages = [&](int bi, int c1, int ln) {
+        const int pr0 = __builtin_amdgcn_readlane(v_fwd, bi);
         const bool pt_ok = pr0 >= 0 && pr0 < a.pt_rows;
         const int npg = (c1 - c0 + kPage - 1) / kPage;
         const int32_t *pt = a.page_table + (int64_t)(pt_ok ? pr0 : 0) * a.pt_stride + c0 / kPage;
-        int v = (pt_ok && lane < npg) ? pt[lane] : -1;
-        job.vpage = (v >= 0 && v < a.num_pages) ? v : -1;
+        return (pt_ok && ln < npg) ? pt[ln] : -1;
+    };
+    int bi_first = kGroupRows, rg_first = 0, gmax_first = 0;
+    for (int bi = 0; bi < kGroupRows; ++bi) {
+        int rg, gmax;
+        if (group_at(bi, rg, gmax)) { bi_first = bi; rg_first = rg; gmax_first = gmax; break; }
     }
-
-    switch (nrows) {   // every wave, also one with no groups (q staging)
-    case 4: score_rows<4>(a, job, lds_sc, (unsigned char *)lds_cnt); break;
-    case 3: score_rows<3>(a, job, lds_sc, (unsigned char *)lds_cnt); break;
-    case 2: score_rows<2>(a, job, lds_sc, (unsigned char *)lds_cnt); break;
-    default: score_rows<1>(a, job, lds_sc, (unsigned char *)lds_cnt); break;
-    }
-
-    // ---- write the chunk's scores (coalesced, 16 bytes per lane when the
-    // score rows allow it) and add the first-digit counts to the row totals
-    __syncthreads();
-    if (kHist) {   // q is no longer needed: the region becomes the counters
-        u32x4_t *c4 = (u32x4_t *)lds_cnt;
-        for (int i = threadIdx.x; i < kHistLds / 4; i += kScoreThreads) c4[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if (bi_first == kGroupRows) return;
+    // the first group's page ids go out before anything waits: page table ->
+    // keys is the longest chain of dependent loads in the set-up
+    const int v_pages_first = load_pages(bi_first, min(c0 + a.chunk, gmax_first), lane);
+    // q staged with the block serves the first group when its rows lie in the block
+    const bool staged_first = bi_first + rg_first <= kGroupRows;
+    if (staged_first) {
+#pragma unroll
+        for (int c = 0; c < kBlockPieces; ++c) {
+            const int ci = threadIdx.x + c * kScoreThreads;
+            *(u32x4_t *)((unsigned char *)lds_cnt + q_lds_off(ci >> 10, (ci >> 4) & 63, ci & 15)) = qt_blk[c];
+        }
         __syncthreads();
     }
+
     const bool vec4 = (((uintptr_t)a.scores | (uintptr_t)(a.sstride * 4)) & 15) == 0;
-    for (int r = 0; r < rg; ++r) {
-        // keys of this row in the chunk (none when its bound lies before c0)
-        const int n = max(min(c1, __builtin_amdgcn_readlane(v_bnd, r)) - c0, 0);
-        float *dst = a.scores + (int64_t)(r0 + r) * a.sstride + c0;
-        const float *src = lds_sc + r * a.chunk;
-        uint32_t *cnt = kHist ? lds_cnt + r * kBins1 * 64 : nullptr;
-        auto count = [&](float x) {
-            const uint32_t d = radix_key(x) >> kDigit1Shift;
-            atomicAdd(cnt + d * 64 + ((lane + d) & 63), 1u);
-        };
-        int done = 0;
-        if (vec4) {
-            done = n & ~3;
-            for (int jx = 4 * (int)threadIdx.x; jx < done; jx += 4 * kScoreThreads) {
-                const f32x4_t x = *(const f32x4_t *)(src + jx);
-                *(f32x4_t *)(dst + jx) = x;
-                if (kHist) { count(x[0]); count(x[1]); count(x[2]); count(x[3]); }
+    for (int bi = bi_first; bi < kGroupRows; ++bi) {
+        int rg, gmax;
+        if (bi == bi_first) { rg = rg_first; gmax = gmax_first; }
+        else if (!group_at(bi, rg, gmax)) continue;
+        const int r0 = yb + bi;
+        const int c1 = min(c0 + a.chunk, gmax);
+        if (bi != bi_first) __syncthreads();   // the previous group's write-out is done with LDS
+        // the thread index passes through an empty asm per group: what the
+        // group's code derives from it (LDS and key offsets) is recomputed in
+        // each group instead of being kept live across all of them
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+
+        // ---- wave roles: the four waves take every fourth 16-key group of
+        // the chunk, each for all of the group's rows
+        const int nrows = rg, part = wave, parts = 4;
+        WaveJob job;
+        job.tid = tid;
+        job.lane = tid & 63;
+        job.c0 = c0;
+        job.chunk = a.chunk;
+        job.slot0 = 0;
+        job.row0 = r0;
+#pragma unroll
+        for (int r = 0; r < kGroupRows; ++r) job.bnd[r] = r < nrows ? __builtin_amdgcn_readlane(v_bnd, bi + r) : 0;
+        const int myend = min(c1, max(max(job.bnd[0], job.bnd[1]), max(job.bnd[2], job.bnd[3])));
+        job.g_first = c0 / kKeysPerMfma + part;
+        job.parts = parts;
+        const int g_end = (myend + kKeysPerMfma - 1) / kKeysPerMfma;
+        job.n_my = job.g_first < g_end ? (g_end - job.g_first + parts - 1) / parts : 0;
+        const int v = bi == bi_first ? v_pages_first : load_pages(bi, c1, job.lane);
+        job.vpage = (v >= 0 && v < a.num_pages) ? v : -1;
+        const bool staged = bi == bi_first && staged_first;
+        const int q_slot = staged ? bi : 0;
+
+        switch (nrows) {   // every wave, also one with no groups (q staging)
+        case 4: score_rows<4>(a, job, lds_sc, (unsigned char *)lds_cnt, q_slot, staged, w_blk); break;
+        case 3: score_rows<3>(a, job, lds_sc, (unsigned char *)lds_cnt, q_slot, staged, w_blk); break;
+        case 2: score_rows<2>(a, job, lds_sc, (unsigned char *)lds_cnt, q_slot, staged, w_blk); break;
+        default: score_rows<1>(a, job, lds_sc, (unsigned char *)lds_cnt, q_slot, staged, w_blk); break;
+        }
+
+        // ---- write the chunk's scores (coalesced, 16 bytes per lane when
+        // the score rows allow it) and add the first-digit counts to the row
+        // totals
+        __syncthreads();
+        if (kHist) {   // q is no longer needed: the region becomes the counters
+            u32x4_t *c4 = (u32x4_t *)lds_cnt;
+            const uint32_t z = (uint32_t)tid >> 16;   // 0, built here rather than kept live
+            for (int i = tid; i < kHistLds / 4; i += kScoreThreads) c4[i] = u32x4_t{z, z, z, z};
+            __syncthreads();
+        }
+        for (int r = 0; r < rg; ++r) {
+            // keys of this row in the chunk (none when its bound lies before c0)
+            const int n = max(min(c1, __builtin_amdgcn_readlane(v_bnd, bi + r)) - c0, 0);
+            float *dst = a.scores + (int64_t)(r0 + r) * a.sstride + c0;
+            const float *src = lds_sc + r * a.chunk;
+            uint32_t *cnt = kHist ? lds_cnt + r * kBins1 * 64 : nullptr;
+            auto count = [&](float x) {
+                const uint32_t d = radix_key(x) >> kDigit1Shift;
+                atomicAdd(cnt + d * 64 + ((job.lane + d) & 63), 1u);
+            };
+            int done = 0;
+            if (vec4) {
+                done = n & ~3;
+                for (int jx = 4 * tid; jx < done; jx += 4 * kScoreThreads) {
+                    const f32x4_t x = *(const f32x4_t *)(src + jx);
+                    *(f32x4_t *)(dst + jx) = x;
+                    if (kHist) { count(x[0]); count(x[1]); count(x[2]); count(x[3]); }
+                }
+            }
+            for (int jx = done + tid; jx < n; jx += kScoreThreads) {
+                const float x = src[jx];
+                dst[jx] = x;
+                if (kHist) count(x);
             }
         }
-        for (int jx = done + (int)threadIdx.x; jx < n; jx += kScoreThreads) {
-            const float x = src[jx];
-            dst[jx] = x;
-            if (kHist) count(x);
-        }
-    }
-    if (kHist) __syncthreads();
-    if (kHist) {
-        const int hr = threadIdx.x >> 6;   // row slot; lane = digit
-        if (hr < rg) {
-            const uint32_t *cnt = lds_cnt + (hr * kBins1 + lane) * 64;
-            uint32_t c = 0;
+        if (kHist) {
+            __syncthreads();
+            const int hr = tid >> 6;   // row slot; lane = digit
+            if (hr < rg) {
+                const uint32_t *cnt = lds_cnt + (hr * kBins1 + job.lane) * 64;
+                uint32_t c = 0;
 #pragma unroll 16
-            for (int i = 0; i < 64; ++i) c += cnt[(i + lane) & 63];
-            if (c) atomicAdd(a.hist1 + ((int64_t)(r0 + hr) * kHist1Slots + blockIdx.x % kHist1Slots) * kBins1 + lane, c);
+                for (int i = 0; i < 64; ++i) c += cnt[(i + job.lane) & 63];
+                if (c) atomicAdd(a.hist1 + ((int64_t)(r0 + hr) * kHist1Slots + blockIdx.x % kHist1Slots) * kBins1 + job.lane, c);
+            }
         }
     }
 }
@@ -506,7 +587,7 @@ void score_kernel(ScoreArgs a) {
 hipError_t launch_score(const ScoreArgs &a, hipStream_t st) {
     if (a.max_bound <= 0) return hipSuccess;
     const int nchunks = (a.max_bound + a.chunk - 1) / a.chunk;
-    dim3 grid(nchunks, a.rows);
+    dim3 grid(nchunks, (a.rows + kGroupRows - 1) / kGroupRows);
     const size_t lds = (size_t)kGroupRows * a.chunk * sizeof(float) + kHistLds * sizeof(uint32_t);
     if (a.hist1)
         hipLaunchKernelGGL(score_kernel<true>, grid, dim3(kScoreThreads), lds, st, a);

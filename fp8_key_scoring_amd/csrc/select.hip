@@ -19,8 +19,10 @@
 // back the whole L2 of an XCD, which costs far more than a dependent launch):
 //   hist1    (only for indexer_topk) first-digit counts of stored scores;
 //   refine   second-digit counts inside the first-digit bin, added to the
-//            row's histogram with one atomic per non-empty bin per workgroup;
-//   gather   every workgroup derives the same split from the two histograms,
+//            row's histogram with one atomic per non-empty bin per workgroup
+//            (the first workgroup also records the first-digit bin);
+//   gather   every workgroup derives the same split from that bin and the
+//            second-digit histogram,
 //            writes its sure keys and its candidates, each in index order, to
 //            its own slices of the workspace (ballot prefix sums, no
 //            atomics), and adds its candidates' third digits to the row's
@@ -117,19 +119,26 @@ __device__ uint32_t block_scan(uint32_t v, uint32_t *wsum, uint32_t *total) {
 }
 
 // Radix keys of keys base + j*kSelThreads + t (j < kSelUnroll) into
-// registers; every load is issued before any is used.  Keys at or past s1 are
-// not read (their slot gets key 0; callers test the position).
-__device__ __forceinline__ void load_keys(const float *row, int64_t base, int64_t s1,
-                                          uint32_t (&u)[kSelUnroll]) {
+// registers; every load is issued before any is used.  Positions at or past
+// s1 (> base) re-read key s1 - 1, so no load sits behind a branch; callers
+// test the position.
+__device__ __forceinline__ void load_raw(const float *row, int64_t base, int64_t s1, float (&v)[kSelUnroll]) {
     const int t = threadIdx.x;
-    float v[kSelUnroll];
 #pragma unroll
     for (int j = 0; j < kSelUnroll; ++j) {
         const int64_t s = base + j * kSelThreads + t;
-        v[j] = s < s1 ? row[s] : 0.0f;
+        v[j] = row[s < s1 ? s : s1 - 1];
     }
+}
+__device__ __forceinline__ void to_keys(const float (&v)[kSelUnroll], uint32_t (&u)[kSelUnroll]) {
 #pragma unroll
     for (int j = 0; j < kSelUnroll; ++j) u[j] = radix_key(v[j]);
+}
+__device__ __forceinline__ void load_keys(const float *row, int64_t base, int64_t s1,
+                                          uint32_t (&u)[kSelUnroll]) {
+    float v[kSelUnroll];
+    load_raw(row, base, s1, v);
+    to_keys(v, u);
 }
 
 // Bitonic sort of v[0..n) in LDS (n a power of two <= 4096), runtime loops.
@@ -163,13 +172,19 @@ __device__ __forceinline__ int clamp_bound(int b, int max_bound) {
     return b < 0 ? 0 : (b > max_bound ? max_bound : b);
 }
 
-// Row r's count in first-digit bin `bin`: the sum of its kHist1Slots copies.
-__device__ __forceinline__ uint32_t hist1_total(const SelectArgs &a, int r, int bin) {
+// Row r's count in first-digit bin `bin` is the sum of its kHist1Slots
+// copies: loaded by hist1_load, summed by hist1_sum (split so that other
+// loads can be issued in between).
+__device__ __forceinline__ void hist1_load(const SelectArgs &a, int r, int bin, uint32_t (&c)[kHist1Slots]) {
     const uint32_t *h = (const uint32_t *)(a.ws + a.L.hist1) + (int64_t)r * kHist1Slots * kBins1 + bin;
-    uint32_t c = 0;
 #pragma unroll
-    for (int s = 0; s < kHist1Slots; ++s) c += h[s * kBins1];
-    return c;
+    for (int s = 0; s < kHist1Slots; ++s) c[s] = h[s * kBins1];
+}
+__device__ __forceinline__ uint32_t hist1_sum(const uint32_t (&c)[kHist1Slots]) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int s = 0; s < kHist1Slots; ++s) v += c[s];
+    return v;
 }
 
 // ---------------------------------------------------------------- hist1
@@ -217,15 +232,29 @@ __global__ __launch_bounds__(kSelThreads) void refine_kernel(SelectArgs a) {
     const int64_t s1 = min(s0 + a.L.sel_chunk, (int64_t)b);
     const float *row = a.scores + (int64_t)r * a.sstride;
 
-    uint32_t u[kSelUnroll];
-    load_keys(row, s0, s1, u);   // the first step's loads overlap the digit search
-    if (t < kBins1) h1[t] = hist1_total(a, r, t);
+    // the first-digit counts are loaded before the first step's keys: loads
+    // complete in order, so the digit search then waits on the counts alone
+    // while the keys are in flight
+    uint32_t c1[kHist1Slots] = {};
+    if (wave == 0) hist1_load(a, r, lane, c1);
+    __builtin_amdgcn_sched_barrier(0);
+    float v0[kSelUnroll];
+    load_raw(row, s0, s1, v0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t < kBins1) h1[t] = hist1_sum(c1);
     for (int i = t; i < kWaves * kBins2; i += kSelThreads) (&h2[0][0])[i] = 0;
     if (t == 0) { sb1 = 0; sabove1 = 0; }
     __syncthreads();
     if (t < 64) wave_find_bin(h1, 1, k, lane, &sb1, &sabove1);
     __syncthreads();
     const uint32_t b1 = (uint32_t)sb1;
+    if (x == 0 && t == 0) {   // the split's first half, for gather
+        RowState *st = (RowState *)(a.ws + a.L.state) + r;
+        st->b1 = b1;
+        st->above1 = sabove1;
+    }
+    uint32_t u[kSelUnroll];
+    to_keys(v0, u);
     for (int64_t base = s0; base < s1; base += kSelTile) {
         if (base != s0) load_keys(row, base, s1, u);
 #pragma unroll
@@ -246,12 +275,11 @@ __global__ __launch_bounds__(kSelThreads) void refine_kernel(SelectArgs a) {
 // writes its sure keys and candidates (each ascending) to its own slices and
 // counts the candidates' third digits.
 __global__ __launch_bounds__(kSelThreads) void gather_kernel(SelectArgs a) {
-    __shared__ uint32_t h1[kBins1];
     __shared__ uint32_t h2[kBins2];
     __shared__ uint32_t h3[kBins3];
     __shared__ uint32_t cs[kSelUnroll * kWaves], cc[kSelUnroll * kWaves];
-    __shared__ int sb1, sb2;
-    __shared__ uint32_t sabove1, sabove2, tot_s, tot_c;
+    __shared__ int sb2;
+    __shared__ uint32_t sabove2, tot_s, tot_c;
     const int r = blockIdx.y, x = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int b = clamp_bound(a.row_bound[r], a.max_bound);
     const int k = a.topk;
@@ -268,34 +296,43 @@ __global__ __launch_bounds__(kSelThreads) void gather_kernel(SelectArgs a) {
     const int64_t s0 = (int64_t)x * a.L.sel_chunk;
     const int64_t s1 = min(s0 + a.L.sel_chunk, (int64_t)b);
 
-    uint32_t u[kSelUnroll];
-    if (s0 < s1) load_keys(row, s0, s1, u);   // overlaps the split below
-    // ---- the split: (b1, above1) from the first digit, (b2, above2) from the second
-    if (t < kBins1) h1[t] = hist1_total(a, r, t);
+    // ---- the split: (b1, above1) as refine found them, (b2, above2) from
+    // the second digit.  The state and counts are loaded before the first
+    // step's keys (loads complete in order), so the split waits on them
+    // alone and the key loads overlap it.  Every thread loads, so no load
+    // sits behind a branch and the waits stay exact.
+    const RowState *st_in = (const RowState *)(a.ws + a.L.state) + r;
+    const uint32_t b1 = st_in->b1, above1 = st_in->above1;
+    const uint32_t c2 = ((const uint32_t *)(a.ws + a.L.hist2))[(int64_t)r * kBins2 + (t & (kBins2 - 1))];
+    __builtin_amdgcn_sched_barrier(0);
+    float v0[kSelUnroll];
+    load_raw(row, s0, s1, v0);   // (b > k >= 1, so key s1 - 1 exists also when s0 >= s1)
+    __builtin_amdgcn_sched_barrier(0);
     if (t < kBins2) {
-        h2[t] = ((const uint32_t *)(a.ws + a.L.hist2))[(int64_t)r * kBins2 + t];
+        h2[t] = c2;
         h3[t] = 0;
     }
-    if (t == 0) { sb1 = 0; sabove1 = 0; sb2 = 0; sabove2 = 0; }
+    if (t == 0) { sb2 = 0; sabove2 = 0; }
     __syncthreads();
-    if (t < 64) wave_find_bin(h1, 1, (uint32_t)k, lane, &sb1, &sabove1);
+    if (t < 64) wave_find_bin(h2, kBins2 / 64, (uint32_t)k - above1, lane, &sb2, &sabove2);
     __syncthreads();
-    if (t < 64) wave_find_bin(h2, kBins2 / 64, (uint32_t)k - sabove1, lane, &sb2, &sabove2);
-    __syncthreads();
-    const uint32_t b1 = (uint32_t)sb1, b2 = (uint32_t)sb2;
+    const uint32_t b2 = (uint32_t)sb2;
     const uint32_t T14 = (b1 << kDigit2Bits) | b2;
     if (x == 0 && t == 0) {
         RowState st;
         st.b1 = b1;
         st.b2 = b2;
-        st.sure = sabove1 + sabove2;
+        st.sure = above1 + sabove2;
         st.need = (uint32_t)k - st.sure;
         st.cand = h2[b2];
-        st.pad[0] = st.pad[1] = st.pad[2] = 0;
+        st.above1 = above1;
+        st.pad[0] = st.pad[1] = 0;
         ((RowState *)(a.ws + a.L.state))[r] = st;
     }
 
     uint32_t ws_ = 0, wc_ = 0;   // sure keys / candidates of this workgroup so far
+    uint32_t u[kSelUnroll];
+    if (s0 < s1) to_keys(v0, u);
     for (int64_t base = s0; base < s1; base += kSelTile) {
         if (base != s0) load_keys(row, base, s1, u);
         // pass 1: counts per (step j, wave), in key order; third digits of candidates

@@ -48,6 +48,13 @@ SMALL = [
     ("unaligned_groups", [3000, 9000], [(0, 3000), (0, 2999), (1, 9000), (1, 8999), (1, 8998), (1, 8997)]),
     ("many_requests", [2500 + 977 * i for i in range(10)],
      [rw for i in range(10) for rw in syn.verify_rows(i, 2500 + 977 * i)]),
+    # one request's run of 70 rows: groups of rows 64.. find their run start
+    # more than 60 rows back
+    ("long_run_70_rows", [2200], [(0, 2200 - j) for j in range(70)]),
+    # runs of 1, 3, 5 and 2 rows: blocks of four rows holding several group
+    # starts, groups reaching into the next block
+    ("mixed_runs", [3100, 4100, 5100, 2600],
+     [(0, 3100), (1, 4100), (1, 4099), (1, 4098)] + [(2, 5100 - j) for j in range(5)] + [(3, 2600), (3, 2599)]),
 ]
 
 
