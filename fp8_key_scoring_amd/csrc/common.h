@@ -26,7 +26,9 @@ constexpr int kSelUnroll = 8;                       // scores in flight per thre
 constexpr int kSelTile = kSelThreads * kSelUnroll;  // keys per workgroup step
 constexpr int kSelMaxWgs = 64;                      // selection workgroups per row (at most)
 constexpr int kCandSlice = 1024;                    // candidates one gather workgroup keeps
+constexpr int kSliceCap = kMaxTopk + kCandSlice;    // entries (sure keys + candidates) per gather workgroup
 constexpr int kCandCap = 4096;                      // candidates one row may have (else fallback)
+constexpr int kEntCap = kMaxTopk + kCandCap;        // entries of one row finalize holds
 constexpr int kTieCap = 1024;                       // keys in the third-digit bin finalize ranks
 constexpr int kZeroRows = 1024;    // rows the zero block is laid out for (at least)
 constexpr int kDigit1Bits = 6;      // first radix digit (counted while scoring)
@@ -67,10 +69,9 @@ struct WsLayout {
     size_t hist2;      // u32 [rz][256]     second-digit counts inside the first-digit bin
     size_t hist3;      // u32 [rz][256]     third-digit counts of the candidates
     size_t state;      // RowState [rows]
-    size_t sure_cnt;   // u32 [rows][sel_wgs]              sure keys per gather workgroup
-    size_t cand_cnt;   // u32 [rows][sel_wgs]              candidates per gather workgroup
-    size_t sure_list;  // i32 [rows][sel_wgs][kMaxTopk]    their indices, ascending
-    size_t cand_list;  // u64 [rows][sel_wgs][kCandSlice]  key << 32 | index, ascending index
+    size_t ent_cnt;    // u32 [rows][sel_wgs]              entries (sure keys + candidates) per gather workgroup
+    size_t cand_cnt;   // u32 [rows][sel_wgs]              candidates among them
+    size_t ent_list;   // u64 [rows][sel_wgs][kSliceCap]   entries in ascending index: key << 32 | sure << 31 | index
     size_t scores;     // f32 [rows][sstride]  (only when the caller gives none)
     size_t total;
     int sel_wgs;
@@ -97,10 +98,9 @@ inline WsLayout ws_layout(int rows, int max_bound, bool own_scores) {
     L.hist2 = take(rz * kBins2 * 4);
     L.hist3 = take(rz * kBins3 * 4);
     L.state = take((size_t)rows * sizeof(RowState));
-    L.sure_cnt = take((size_t)rows * n * 4);
+    L.ent_cnt = take((size_t)rows * n * 4);
     L.cand_cnt = take((size_t)rows * n * 4);
-    L.sure_list = take((size_t)rows * n * kMaxTopk * 4);
-    L.cand_list = take((size_t)rows * n * kCandSlice * 8);
+    L.ent_list = take((size_t)rows * n * kSliceCap * 8);
     L.scores = own_scores ? take((size_t)rows * (size_t)L.sstride * 4) : off;
     L.total = off;
     return L;

@@ -22,17 +22,17 @@
 //            row's histogram with one atomic per non-empty bin per workgroup
 //            (the first workgroup also records the first-digit bin);
 //   gather   every workgroup derives the same split from that bin and the
-//            second-digit histogram,
-//            writes its sure keys and its candidates, each in index order, to
-//            its own slices of the workspace (ballot prefix sums, no
-//            atomics), and adds its candidates' third digits to the row's
-//            third histogram;
-//   finalize one workgroup per row: the third digit's bin of the k-th key
+//            second-digit histogram, writes its sure keys and candidates as
+//            one list in index order to its own slice of the workspace
+//            (ballot prefix sums, no atomics; a flag marks the sure keys),
+//            and adds its candidates' third digits to the row's third
+//            histogram;
+//   finalize one workgroup per row: the slices, concatenated, are the row's
+//            entries in index order; the third digit's bin of the k-th key
 //            splits the candidates once more; all above it are taken, the few
 //            inside it are ranked by (key desc, index asc); a stable
-//            compaction keeps index order, and a merge by binary search with
-//            the concatenated sure slices writes the row's output in
-//            ascending index order (deterministic bytes) with no sort.
+//            compaction of the kept entries is the row's output in ascending
+//            index order (deterministic bytes), with no sort and no merge.
 // Workgroups are 1024 threads (four waves per SIMD hide LDS latency) and each
 // thread keeps 8 score loads in flight, so a workgroup's scan of its 8192
 // keys is one memory round trip.  Rows whose candidates overflow the slices
@@ -43,9 +43,8 @@
 namespace fp8idx {
 
 constexpr int kWaves = kSelThreads / 64;
-static_assert(kSelThreads == 1024, "finalize keeps four candidates per thread");
+static_assert(kSelThreads == 1024, "selection workgroups are 16 waves");
 static_assert(kSelUnroll * kWaves == 128, "gather prefix: two entries per lane");
-static_assert(kCandCap == 4 * kSelThreads, "finalize keeps four candidates per thread");
 static_assert(kHist1Slots * kBins1 <= kSelThreads, "finalize clears the first-digit copies in one pass");
 
 __device__ __forceinline__ uint32_t lane_prefix(uint64_t m) {
@@ -139,33 +138,6 @@ __device__ __forceinline__ void load_keys(const float *row, int64_t base, int64_
     float v[kSelUnroll];
     load_raw(row, base, s1, v);
     to_keys(v, u);
-}
-
-// Bitonic sort of v[0..n) in LDS (n a power of two <= 4096), runtime loops.
-template <typename T, bool kAsc>
-__device__ void lds_bitonic(T *v, int n) {
-    const int t = threadIdx.x;
-    for (int kk = 2; kk <= n; kk <<= 1) {
-        for (int j = kk >> 1; j > 0; j >>= 1) {
-            for (int i = t; i < n / 2; i += kSelThreads) {
-                const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
-                const int hi = lo + j;
-                const bool up = ((lo & kk) == 0) == kAsc;
-                const T x = v[lo], y = v[hi];
-                if (up ? (x > y) : (x < y)) { v[lo] = y; v[hi] = x; }
-            }
-            __syncthreads();
-        }
-    }
-}
-
-__device__ __forceinline__ int lower_bound(const int32_t *a, int n, int32_t v) {
-    int lo = 0, hi = n;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (a[mid] < v) lo = mid + 1; else hi = mid;
-    }
-    return lo;
 }
 
 __device__ __forceinline__ int clamp_bound(int b, int max_bound) {
@@ -290,8 +262,7 @@ __global__ __launch_bounds__(kSelThreads) void gather_kernel(SelectArgs a) {
             for (int i = t; i < k; i += kSelThreads) out_row[i] = i < b ? i : -1;
         return;
     }
-    int32_t *slice_s = (int32_t *)(a.ws + a.L.sure_list) + ((int64_t)r * S + x) * kMaxTopk;
-    unsigned long long *slice_c = (unsigned long long *)(a.ws + a.L.cand_list) + ((int64_t)r * S + x) * kCandSlice;
+    unsigned long long *slice_e = (unsigned long long *)(a.ws + a.L.ent_list) + ((int64_t)r * S + x) * kSliceCap;
     const float *row = a.scores + (int64_t)r * a.sstride;
     const int64_t s0 = (int64_t)x * a.L.sel_chunk;
     const int64_t s1 = min(s0 + a.L.sel_chunk, (int64_t)b);
@@ -330,22 +301,22 @@ __global__ __launch_bounds__(kSelThreads) void gather_kernel(SelectArgs a) {
         ((RowState *)(a.ws + a.L.state))[r] = st;
     }
 
-    uint32_t ws_ = 0, wc_ = 0;   // sure keys / candidates of this workgroup so far
+    uint32_t we_ = 0, wc_ = 0;   // entries / candidates of this workgroup so far
     uint32_t u[kSelUnroll];
     if (s0 < s1) to_keys(v0, u);
     for (int64_t base = s0; base < s1; base += kSelTile) {
         if (base != s0) load_keys(row, base, s1, u);
-        // pass 1: counts per (step j, wave), in key order; third digits of candidates
+        // pass 1: entry and candidate counts per (step j, wave), in key
+        // order; third digits of candidates
 #pragma unroll
         for (int j = 0; j < kSelUnroll; ++j) {
             const bool valid = base + j * kSelThreads + t < s1;
             const uint32_t top = u[j] >> kDigit2Shift;
-            const bool sure = valid && top > T14;
             const bool cnd = valid && top == T14;
-            const uint64_t ms = __ballot(sure);
+            const uint64_t me = __ballot(valid && top >= T14);
             const uint64_t mc = __ballot(cnd);
             if (lane == 0) {
-                cs[j * kWaves + wave] = (uint32_t)__popcll(ms);
+                cs[j * kWaves + wave] = (uint32_t)__popcll(me);
                 cc[j * kWaves + wave] = (uint32_t)__popcll(mc);
             }
             if (cnd) atomicAdd(&h3[(u[j] >> kDigit3Shift) & (kBins3 - 1)], 1u);
@@ -354,31 +325,26 @@ __global__ __launch_bounds__(kSelThreads) void gather_kernel(SelectArgs a) {
         if (wave == 0) wave_scan128(cs, &tot_s, lane);
         if (wave == 1) wave_scan128(cc, &tot_c, lane);
         __syncthreads();
-        // pass 2: each key to its place
+        // pass 2: each entry to its place (sure keys carry a flag, candidates
+        // their key)
 #pragma unroll
         for (int j = 0; j < kSelUnroll; ++j) {
             const int64_t s = base + j * kSelThreads + t;
-            const bool valid = s < s1;
             const uint32_t top = u[j] >> kDigit2Shift;
-            const bool sure = valid && top > T14;
-            const bool cnd = valid && top == T14;
-            const uint64_t ms = __ballot(sure);
-            const uint64_t mc = __ballot(cnd);
-            if (sure) {
-                const uint32_t pos = ws_ + cs[j * kWaves + wave] + lane_prefix(ms);
-                if (pos < (uint32_t)kMaxTopk) slice_s[pos] = (int32_t)s;
-            }
-            if (cnd) {
-                const uint32_t pos = wc_ + cc[j * kWaves + wave] + lane_prefix(mc);
-                if (pos < (uint32_t)kCandSlice) slice_c[pos] = ((unsigned long long)u[j] << 32) | (uint32_t)s;
+            const bool ent = s < s1 && top >= T14;
+            const uint64_t me = __ballot(ent);
+            if (ent) {
+                const uint32_t pos = we_ + cs[j * kWaves + wave] + lane_prefix(me);
+                const uint32_t lo = (uint32_t)s | (top > T14 ? 0x80000000u : 0u);
+                if (pos < (uint32_t)kSliceCap) slice_e[pos] = ((unsigned long long)u[j] << 32) | lo;
             }
         }
-        ws_ += tot_s;
+        we_ += tot_s;
         wc_ += tot_c;
         __syncthreads();
     }
     if (t == 0) {
-        ((uint32_t *)(a.ws + a.L.sure_cnt))[(int64_t)r * S + x] = ws_ < (uint32_t)kMaxTopk ? ws_ : (uint32_t)kMaxTopk;
+        ((uint32_t *)(a.ws + a.L.ent_cnt))[(int64_t)r * S + x] = we_;
         ((uint32_t *)(a.ws + a.L.cand_cnt))[(int64_t)r * S + x] = wc_;
     }
     if (t < kBins3 && h3[t]) atomicAdd((uint32_t *)(a.ws + a.L.hist3) + (int64_t)r * kBins3 + t, h3[t]);
@@ -387,10 +353,11 @@ __global__ __launch_bounds__(kSelThreads) void gather_kernel(SelectArgs a) {
 // ------------------------------------------------------------- fallback
 // Exact resolution inside the 14-bit prefix bin by one workgroup rescanning
 // the row, used when the candidates overflow their slices: three more digit
-// passes fix the threshold key T, then keys above T and the first
-// `need - above` ties at T in index order go to ch[0..need) (any order).
-__device__ void fallback_select(const float *row, int b, uint32_t T14, uint32_t need, int32_t *ch,
-                                uint32_t *h, int *sB, uint32_t *sAbove, uint32_t *wtot, uint32_t *spos) {
+// passes fix the threshold key T (the k-th largest); a last pass in index
+// order then writes the keys above T and the first `need - above` ties at T
+// to the row's output, compacted stably (ascending index).
+__device__ void fallback_write(const float *row, int b, uint32_t T14, uint32_t need, int32_t *out_row, int k,
+                               uint32_t *h, int *sB, uint32_t *sAbove, uint32_t *wsel, uint32_t *wtie) {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int shifts[3] = {10, 2, 0};
     const int widths[3] = {8, 8, 2};
@@ -420,47 +387,58 @@ __device__ void fallback_select(const float *row, int b, uint32_t T14, uint32_t 
         __syncthreads();
     }
     const uint32_t T = prefix;   // the k-th largest key; need_cur ties at T to take
-    if (t == 0) *spos = 0;
-    __syncthreads();
-    uint32_t tie_run = 0;
+    uint32_t sel_run = 0, tie_run = 0;
     for (int base = 0; base < b; base += kSelThreads) {
         const int s = base + t;
         const uint32_t u = s < b ? radix_key(row[s]) : 0u;
-        const bool in = s < b && (u >> kDigit2Shift) == T14;
-        const bool gt = in && u > T;
-        const bool tie = in && u == T;
-        const uint64_t m = __ballot(tie);
-        if (lane == 0) wtot[wave] = (uint32_t)__popcll(m);
+        const bool gt = s < b && u > T;
+        const bool tie = s < b && u == T;
+        const uint64_t mt = __ballot(tie);
+        if (lane == 0) wtie[wave] = (uint32_t)__popcll(mt);
         __syncthreads();
-        uint32_t woff = 0, all = 0;
+        uint32_t toff = 0, tall = 0;
         for (int wv = 0; wv < kWaves; ++wv) {
-            if (wv < wave) woff += wtot[wv];
-            all += wtot[wv];
+            if (wv < wave) toff += wtie[wv];
+            tall += wtie[wv];
         }
-        const uint32_t rank = tie_run + woff + lane_prefix(m);
-        if (gt || (tie && rank < need_cur)) {
-            const uint32_t p = atomicAdd(spos, 1u);
-            if (p < need) ch[p] = s;
+        const bool sel = gt || (tie && tie_run + toff + lane_prefix(mt) < need_cur);
+        const uint64_t ms = __ballot(sel);
+        if (lane == 0) wsel[wave] = (uint32_t)__popcll(ms);
+        __syncthreads();
+        uint32_t soff = 0, sall = 0;
+        for (int wv = 0; wv < kWaves; ++wv) {
+            if (wv < wave) soff += wsel[wv];
+            sall += wsel[wv];
         }
-        tie_run += all;
+        if (sel) {
+            const uint32_t pos = sel_run + soff + lane_prefix(ms);
+            if (pos < (uint32_t)k) out_row[pos] = s;
+        }
+        sel_run += sall;
+        tie_run += tall;
         __syncthreads();
     }
 }
 
 // -------------------------------------------------------------- finalize
-// One workgroup per row: choose the `need` candidates, merge them with the
-// sure keys into the row's output in ascending index order, and leave the
-// row's histograms zeroed.
+// One workgroup per row.  The slices' entries (sure keys and candidates, each
+// slice in ascending index, slices in index order) are gathered into LDS in
+// one ascending list; the third digit's bin of the k-th key splits the
+// candidates once more (all above it are taken, the few inside it ranked by
+// key desc, index asc); a stable compaction of the kept entries is the row's
+// output in ascending index order.  The row's histograms are left zeroed.
 __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
+    __shared__ unsigned long long ent[kEntCap];   // the row's entries, ascending index
     __shared__ unsigned long long tie[kTieCap];   // candidates inside the third-digit bin
-    __shared__ unsigned long long cand[kCandCap]; // all candidates (key << 32 | index), ascending index
-    __shared__ int32_t su[kMaxTopk];              // sure keys, ascending
-    __shared__ int32_t chs[kMaxTopk];             // chosen candidates, ascending
-    __shared__ uint32_t offs[kSelMaxWgs + 1], offc[kSelMaxWgs + 1];
+    __shared__ uint32_t offe[kSelMaxWgs + 1];
     __shared__ uint32_t h3[kBins3];
-    __shared__ uint32_t wsum[kWaves];
+    __shared__ uint32_t wsum[kWaves], wtie[kWaves];
     __shared__ int sB;
-    __shared__ uint32_t sAbove, ntie, ovf, total, spos;
+    __shared__ uint32_t sAbove, ntie, ovf, total;
+    constexpr int kPer = kEntCap / kSelThreads;   // entries per thread
+    constexpr int kPre = 4;                       // entries per thread loaded ahead of the counts
+    static_assert(kEntCap % kSelThreads == 0, "finalize: whole entries per thread");
+    static_assert(kSelMaxWgs * 16 == kSelThreads, "finalize: 16 threads per slice");
     const int r = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int b = clamp_bound(a.row_bound[r], a.max_bound);
     const int k = a.topk;
@@ -468,70 +446,68 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
     int32_t *out_row = a.out_idx + (int64_t)r * k;
     uint32_t *hist3 = (uint32_t *)(a.ws + a.L.hist3) + (int64_t)r * kBins3;
     if (b > k) {
-        const RowState st = ((const RowState *)(a.ws + a.L.state))[r];
-        const uint32_t *scnt = (const uint32_t *)(a.ws + a.L.sure_cnt) + (int64_t)r * S;
+        const uint32_t *ecnt = (const uint32_t *)(a.ws + a.L.ent_cnt) + (int64_t)r * S;
         const uint32_t *ccnt = (const uint32_t *)(a.ws + a.L.cand_cnt) + (int64_t)r * S;
-        const int32_t *sl_s = (const int32_t *)(a.ws + a.L.sure_list) + (int64_t)r * S * kMaxTopk;
-        const unsigned long long *sl_c = (const unsigned long long *)(a.ws + a.L.cand_list) + (int64_t)r * S * kCandSlice;
+        const unsigned long long *sl = (const unsigned long long *)(a.ws + a.L.ent_list) + (int64_t)r * S * kSliceCap;
+        // Every load goes out before any is waited on: the state, the third
+        // digits, the per-slice counts and, without waiting for those, the
+        // first 64 entries of every slice (16 threads per slice), which is
+        // all of a slice in the usual case.
+        const int x = t >> 4, j0 = t & 15;
+        const int xs = x < S ? x : 0;
+        const RowState st = ((const RowState *)(a.ws + a.L.state))[r];
+        const uint32_t h3v = hist3[t & (kBins3 - 1)];
+        const uint32_t ne = ecnt[lane < S ? lane : 0], ncx = ccnt[lane < S ? lane : 0];
+        unsigned long long pre[kPre];
+#pragma unroll
+        for (int m = 0; m < kPre; ++m) pre[m] = sl[(int64_t)xs * kSliceCap + j0 + 16 * m];
+        __builtin_amdgcn_sched_barrier(0);
         const int need = (int)(st.need < (uint32_t)kMaxTopk ? st.need : (uint32_t)kMaxTopk);
         const uint32_t T14 = (st.b1 << kDigit2Bits) | st.b2;
-        // slice offsets (exclusive prefix of the per-workgroup counts)
-        if (wave < 2) {
-            const uint32_t c = lane < S ? (wave == 0 ? scnt[lane] : ccnt[lane]) : 0u;
-            const uint64_t big = __ballot(wave == 1 && c > (uint32_t)kCandSlice);
-            uint32_t incl = c;
+        // slice offsets (exclusive prefix of the entry counts); candidates
+        // past a slice's capacity or the row's send the row to the fallback
+        if (wave == 0) {
+            const uint32_t c = lane < S ? ne : 0u, cc = lane < S ? ncx : 0u;
+            const uint64_t big = __ballot(cc > (uint32_t)kCandSlice);
+            uint32_t incl = c, cincl = cc;
             for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t v = __shfl_up(incl, o);
-                if (lane >= o) incl += v;
+                const uint32_t v = __shfl_up(incl, o), w = __shfl_up(cincl, o);
+                if (lane >= o) { incl += v; cincl += w; }
             }
-            uint32_t *off = wave == 0 ? offs : offc;
-            off[lane] = incl - c;
+            offe[lane] = incl - c;
             if (lane == 63) {
-                off[kSelMaxWgs] = incl;
-                if (wave == 1) ovf = (big != 0ull) || incl > (uint32_t)kCandCap;
+                offe[kSelMaxWgs] = incl;
+                ovf = (big != 0ull) || cincl > (uint32_t)kCandCap || incl > (uint32_t)kEntCap;
             }
         }
-        if (t < kBins3) h3[t] = hist3[t];
+        if (t < kBins3) h3[t] = h3v;
         if (t == 0) { sB = 0; sAbove = 0; ntie = 0; }
         __syncthreads();
-        const int ns = (int)min(offs[kSelMaxWgs], (uint32_t)(k - need));
-        const int nc = (int)offc[kSelMaxWgs];
+        const int N = (int)offe[kSelMaxWgs];
         bool overflow = ovf != 0u;
-        // The slices' lists, concatenated in workgroup order (ascending key
-        // index), are copied to LDS: 16 threads per slice, each taking every
-        // 16th entry, so every load address is known without a search.
-        {
-            const int x = t >> 4, j0 = t & 15;
-            if (x < S) {
-                const int nsx = (int)min(scnt[x], (uint32_t)kMaxTopk);
-                const int o = (int)offs[x];
-                for (int jj = j0; jj < nsx; jj += 16)
-                    if (o + jj < ns) su[o + jj] = sl_s[(int64_t)x * kMaxTopk + jj];
-                if (!overflow) {
-                    const int ncx = (int)ccnt[x];
-                    const int oc = (int)offc[x];
-                    for (int jj = j0; jj < ncx; jj += 16)
-                        cand[oc + jj] = sl_c[(int64_t)x * kCandSlice + jj];
-                }
-            }
-        }
-        __syncthreads();
-        unsigned long long c[4];
+        unsigned long long e[kPer];
         if (!overflow) {
-            // this thread's candidates t*4 .. t*4+3 (ascending index)
+            if (x < S) {
+                const int o = (int)offe[x], n = (int)(offe[x + 1] - offe[x]);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int i = t * 4 + q;
-                c[q] = i < nc ? cand[i] : 0ull;
+                for (int m = 0; m < kPre; ++m)
+                    if (j0 + 16 * m < n) ent[o + j0 + 16 * m] = pre[m];
+                for (int jj = j0 + 16 * kPre; jj < n; jj += 16) ent[o + jj] = sl[(int64_t)x * kSliceCap + jj];
             }
             if (t < 64) wave_find_bin(h3, kBins3 / 64, (uint32_t)need, lane, &sB, &sAbove);
             __syncthreads();
             const uint32_t T22 = (T14 << kDigit3Bits) | (uint32_t)sB;
+            // this thread's entries t*kPer .. t*kPer+kPer-1; candidates in the
+            // third-digit bin are collected for ranking
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (t * 4 + q < nc && (uint32_t)(c[q] >> (32 + kDigit3Shift)) == T22) {
+            for (int q = 0; q < kPer; ++q) {
+                const int i = t * kPer + q;
+                e[q] = i < N ? ent[i] : 0ull;
+                const bool cand_in_bin = i < N && !((uint32_t)e[q] & 0x80000000u) &&
+                                         (uint32_t)(e[q] >> (32 + kDigit3Shift)) == T22;
+                if (cand_in_bin) {
                     const uint32_t p = atomicAdd(&ntie, 1u);
-                    if (p < (uint32_t)kTieCap) tie[p] = c[q];
+                    if (p < (uint32_t)kTieCap) tie[p] = e[q];
                 }
             }
             __syncthreads();
@@ -541,51 +517,41 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
             const uint32_t T22 = (T14 << kDigit3Bits) | (uint32_t)sB;
             const uint32_t need3 = (uint32_t)need - sAbove;
             const int nt = (int)ntie;
-            bool chosen[4];
+            bool kept[kPer];
             uint32_t cnt = 0;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                chosen[q] = false;
-                if (t * 4 + q < nc) {
-                    const uint32_t key = (uint32_t)(c[q] >> 32);
+            for (int q = 0; q < kPer; ++q) {
+                kept[q] = false;
+                if (t * kPer + q < N) {
+                    const uint32_t lo = (uint32_t)e[q];
+                    const uint32_t key = (uint32_t)(e[q] >> 32);
                     const uint32_t d = key >> kDigit3Shift;
-                    if (d > T22) {
-                        chosen[q] = true;
+                    if (lo & 0x80000000u) {   // sure key
+                        kept[q] = true;
+                    } else if (d > T22) {
+                        kept[q] = true;
                     } else if (d == T22) {   // rank inside the bin: larger key first, then lower index
-                        const uint32_t idx = (uint32_t)c[q];
+                        const uint32_t idx = lo;
                         uint32_t rank = 0;
-                        for (int e = 0; e < nt; ++e) {
-                            const uint32_t ek = (uint32_t)(tie[e] >> 32), ei = (uint32_t)tie[e];
+                        for (int f = 0; f < nt; ++f) {
+                            const uint32_t ek = (uint32_t)(tie[f] >> 32), ei = (uint32_t)tie[f];
                             rank += (ek > key) || (ek == key && ei < idx);
                         }
-                        chosen[q] = rank < need3;
+                        kept[q] = rank < need3;
                     }
                 }
-                cnt += chosen[q];
+                cnt += kept[q];
             }
             uint32_t pos = block_scan(cnt, wsum, &total);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (chosen[q] && pos < (uint32_t)kMaxTopk) chs[pos++] = (int32_t)(uint32_t)c[q];
+            for (int q = 0; q < kPer; ++q)
+                if (kept[q]) {
+                    if (pos < (uint32_t)k) out_row[pos] = (int32_t)((uint32_t)e[q] & 0x7FFFFFFFu);
+                    ++pos;
+                }
         } else {
-            fallback_select(a.scores + (int64_t)r * a.sstride, b, T14, (uint32_t)need, chs, h3, &sB,
-                            &sAbove, wsum, &spos);
-            __syncthreads();
-            int n2 = 1;
-            while (n2 < need) n2 <<= 1;
-            for (int i = need + t; i < n2; i += kSelThreads) chs[i] = 0x7FFFFFFF;
-            __syncthreads();
-            lds_bitonic<int32_t, true>(chs, n2);
-        }
-        __syncthreads();
-        // merge: each value's place is its rank in its own list plus its rank in the other
-        for (int p = t; p < ns; p += kSelThreads) {
-            const int32_t v = su[p];
-            out_row[p + lower_bound(chs, need, v)] = v;
-        }
-        for (int j = t; j < need; j += kSelThreads) {
-            const int32_t cj = chs[j];
-            out_row[j + lower_bound(su, ns, cj)] = cj;
+            fallback_write(a.scores + (int64_t)r * a.sstride, b, T14, (uint32_t)need, out_row, k, h3, &sB,
+                           &sAbove, wsum, wtie);
         }
     }
     if (t < kHist1Slots * kBins1) ((uint32_t *)(a.ws + a.L.hist1))[(int64_t)r * kHist1Slots * kBins1 + t] = 0;

@@ -101,6 +101,21 @@ def test_ties_straddling_the_threshold():
     assert np.array_equal(out[0], expect)
 
 
+def test_ties_ranked_inside_the_last_bin():
+    # 1500 keys above the threshold value and 900 keys equal to it: the 900
+    # fit the candidate slices, so the ties are ranked (by index) inside the
+    # third-digit bin rather than by the full rescan
+    p = syn.scale_tie_problem(n=12000, counts=(1500, 900))
+    scores, out = full_check(p, "scale_ties_ranked")
+    s = scores[0, :12000]
+    vals = np.unique(s)
+    top = np.nonzero(s == vals[2])[0]
+    mid = np.nonzero(s == vals[1])[0]
+    assert top.size == 1500 and mid.size == 900
+    expect = np.sort(np.concatenate([top, mid[:2048 - top.size]]))
+    assert np.array_equal(out[0], expect)
+
+
 def test_extreme_codes():
     p = syn.build_problem("extreme", 4, [9000], syn.verify_rows(0, 9000), key_mode="extreme")
     full_check(p, "extreme")
