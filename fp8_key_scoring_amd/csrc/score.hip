@@ -9,31 +9,33 @@
 // first radix digit of every stored score in the scoring pass).
 //
 // Design on gfx950 (not the page's: its kernels are prior art here):
-//  * A workgroup is 4 waves and takes one group of up to 4 rows that share a
-//    page-table row (one request's verify rows) and one chunk of its keys.
-//    With 4 rows each wave owns one row and walks every 16-key group of the
-//    chunk; the four waves read the same key bytes, so HBM sees each key once
-//    and the repeats hit the CU's L1.  With 1 or 2 rows the waves split the
-//    chunk's 16-key groups so no key is read twice per row.
+//  * A workgroup is 4 waves, one per SIMD, each with the whole 512-entry
+//    register file.  It takes the row groups (up to 4 consecutive rows that
+//    share a page-table row: one request's verify rows) that start in its
+//    block of 4 rows, and one chunk of their keys.  Each wave scores all of a
+//    group's rows, so a key is read from HBM once and converted once; wave w
+//    takes page w of every block of four pages of the chunk.
 //  * Per 16-key group a lane loads 32 contiguous code bytes of key lane%16
-//    (two 16-byte loads; the page id comes from a scalar load of the page
-//    table, the rest is a fixed per-lane offset) plus that key's scale.  The
-//    codes go straight to registers, are widened E4M3 -> bf16 (exact) with the
-//    gfx950 packed conversion, and feed the B operand of
-//    v_mfma_f32_16x16x32_bf16 (K = the 128 head dims in 4 steps, N = 16
-//    keys).  The A operand is q, 16 heads per MFMA, held in registers for the
-//    whole chunk (64 VGPRs: 4 head blocks x 4 K steps).  The order in which
-//    head dims feed the K index is a free permutation applied to q and k alike.
-//    (The fp8 x fp8 MFMA is not used: its internal accumulation is far below
-//    fp32 precision, while the bf16 one accumulates in fp32.)
-//  * Epilogue: lane l holds heads 16b + 4(l/16) + j of key l%16 for b, j < 4;
-//    it sums w * max(d, 0) over its 16 heads, two permlane swaps (32 and 16
-//    lanes) finish the sum over the 64 heads, and the key's scale multiplies
-//    the total.  Scores of four consecutive groups are gathered in one
-//    register (lane row i holds group i) and stored by all 64 lanes at once,
-//    masked at the row's bound; the same lanes add the first radix digit of
-//    each stored score to a 64-bin LDS histogram per row, which is added to
-//    the row's global histogram at the end of the workgroup.
+//    (two 16-byte loads from a wave-uniform base: the page id is read from a
+//    register holding the chunk's page ids, the rest is a fixed per-lane
+//    offset) plus that key's scale, four groups ahead.  The codes go straight
+//    to registers, are widened E4M3 -> bf16 (exact) with the gfx950 packed
+//    conversion, and feed the B operand of v_mfma_f32_16x16x32_bf16 (K = the
+//    128 head dims in 4 steps, N = 16 keys).  The A operand is q, 16 heads
+//    per MFMA, held in AGPRs for the whole chunk (64 per row).  The order in
+//    which head dims feed the K index is a free permutation applied to q and
+//    k alike.  (The fp8 x fp8 MFMA is not used: it would need q in fp8.)
+//  * Epilogue: lane l holds heads 16b + 4(l/16) + j of key l%16 for b, j < 4.
+//    max(d, 0) = (d + |d|) / 2: the linear half, (1/2) sum_h w_h d_h, is one
+//    more MFMA block against (1/2) sum_h w_h q_h; the other half is one fma
+//    per head with |d| as a free source modifier.  Two permlane swap rounds
+//    (32 and 16 lanes) finish the sum over the 64 heads for four groups at
+//    once, and the keys' scales multiply the totals.
+//  * Scores leave from registers: after every page of a wave, lane l holds
+//    the score of the page's key l, so each row's 64 scores are one 256-byte
+//    buffer store, masked at the row's bound by the buffer's extent.  When
+//    counting, the same lanes add each score's first radix digit to per-row
+//    LDS counters, which are added to the row's global histogram at the end.
 #include "common.h"
 
 namespace fp8idx {
@@ -65,7 +67,14 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
 // bank, and the reduction (lane = digit, summing its 64 counters) does too.
 constexpr int kHistLds = kGroupRows * kBins1 * 64;   // u32 counters
 constexpr int kBlockPieces = kGroupRows * kHeads * kDim / 8 / kScoreThreads;   // q pieces per thread, 4 rows
-static_assert(kHistLds * 4 == kGroupRows * kHeads * kDim * 2, "the counter region also holds q of four rows");
+// Word 3 of a raw buffer resource for 32-bit accesses (32-bit data format).
+constexpr int kBufferFlags = 0x00020000;
+
+// Dynamic LDS: q of four rows, then the linear term's A operand, then (when
+// counting) the first-digit counters.
+constexpr int kLdsQ = kGroupRows * kHeads * kDim * 2;     // 64 KB
+constexpr int kLdsT1 = 4 * 64 * 8 * 2;                   // [ks][lane][8] bf16, 4 KB
+constexpr int kLdsCnt = kHistLds * 4;                    // 64 KB
 
 // The same pointer, held in scalar registers and opaque to the optimiser:
 // a load from it plus a 32-bit lane offset then uses the scalar-base
@@ -126,20 +135,22 @@ struct KeyGroup {
     int ok;           // wave-uniform: the page id was in range
 };
 
-// What one wave scores: R rows (R = 1..4) over every parts-th 16-key group
-// of the chunk, starting at group g_first.
+// What one wave scores: R rows (R = 1..4) over its share of the chunk's
+// 16-key groups.  The chunk is cut into blocks of 16 groups (4 pages); wave w
+// takes page w of each block, i.e. its i-th group is
+// gbase + 16 * (i / 4) + i % 4 with gbase = (first group of the chunk) + 4w,
+// so every 4 consecutive groups of a wave are one page: 64 consecutive keys.
 struct WaveJob {
     int tid;         // thread index in the workgroup
     int lane;
     int c0;          // first key of the chunk (a multiple of 64)
-    int chunk;       // keys per chunk (row stride of the LDS score buffer)
-    int g_first;     // first 16-key group (index over the request's keys)
-    int parts;       // the wave takes every parts-th group
+    int chunk;       // keys per chunk
+    int gbase;       // the wave's first 16-key group (index over the request's keys)
     int n_my;        // groups the wave takes
     int vpage;       // page id of the chunk's page number `lane` (-1: out of range)
-    int slot0;       // LDS row slot of the wave's first row (0..3)
     int row0;        // the wave's first row
     int bnd[kGroupRows];   // exclusive bounds of the wave's rows
+    __device__ __forceinline__ int group(int i) const { return gbase + 16 * (i >> 2) + (i & 3); }
 };
 
 // Scores R rows of one wave.  A "unit" is (group, row); units run in order
@@ -148,9 +159,10 @@ struct WaveJob {
 // row) the conversion of the next group and the refill of its ring slot are
 // independent, and the scheduler interleaves them: one MFMA, then a few VALU
 // ops.  A group's keys are converted once and used by all R rows.
-template <int R>
-__device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j, float *lds_sc,
-                                           unsigned char *lds_q, int q_slot, bool staged, float w_blk) {
+template <int R, bool kHist>
+__device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j, unsigned char *lds_q,
+                                           bf16_t *t1_lds, uint32_t *lds_cnt, int q_slot, bool staged,
+                                           float w_blk) {
     constexpr int kRing = ring_depth<R>();
     const int lane = j.lane;
     const int kig = lane & 15;      // key of the group this lane loads / scores
@@ -164,7 +176,7 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
     // 32-bit offset.
     auto load_group = [&](int i, KeyGroup &kg) {
         const int ic = max(min(i, j.n_my - 1), 0);   // in range also when n_my == 0
-        const int g = j.g_first + ic * j.parts;
+        const int g = j.group(ic);
         const int page = __builtin_amdgcn_readlane(j.vpage, (g - gc0) >> 2);
         kg.ok = page >= 0;
         const int64_t key0 = (int64_t)(kg.ok ? page : 0) * kPage + (g & 3) * kKeysPerMfma;
@@ -213,9 +225,7 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
         // into three bf16 parts hi + mid + lo (each residual exact in fp32,
         // so the three carry u_r to fp32 precision); the other rows are zero.
         // Wave q_slot + r computes row r, lane l dims 2l and 2l+1, from q in
-        // LDS and w[r][h] broadcast from lane h.  Written to the score stage,
-        // which is free until the first flush.
-        bf16_t *t1_lds = (bf16_t *)lds_sc;   // [ks][lane][8]
+        // LDS and w[r][h] broadcast from lane h, through LDS ([ks][lane][8]).
         const int ur = wave_idx - q_slot;
         if (ur >= 0 && ur < R) {
             const float w_lane = staged ? w_blk : a.w[(int64_t)(j.row0 + ur) * kHeads + lane];
@@ -255,7 +265,7 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
             const bf16x8_t v = *(const bf16x8_t *)(t1_lds + (ks * 64 + lane) * 8);
             t1a[ks] = t1_row ? v : bf16x8_t{};
         }
-        __syncthreads();   // the score stage is written from here on
+        __syncthreads();   // t1_lds may be written again by the next row group
     }
     if (j.n_my == 0) return;
     // q lives in AGPRs: the MFMA reads its A operand from there directly,
@@ -320,14 +330,32 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
     // when the first group of the next block is taken, which happens one
     // step before the flush of the complete block.
     float sv_fill = 0.0f, sv_done = 0.0f;
-    auto flush = [&](int g) {   // g: last group of the block
+    // A block is one page of the wave: lane l holds the score of key
+    // (first key of the page) + l, so each row's 64 scores go out as one
+    // 256-byte store, masked at the row's bound, and (when counting) each
+    // lane adds its score's first radix digit to the row's LDS counters at
+    // position (lane + digit) % 64.
+    auto flush = [&](int g) {   // g: the wave's index of the block's last group
         const int iq = g - 3 + lrow;
-        const int s = (j.g_first + iq * j.parts) * kKeysPerMfma + kig;
+        const int s = j.group(iq) * kKeysPerMfma + kig;
+        const bool in_job = iq >= 0 && iq < j.n_my;
         const float scl = sv_done;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const float out = reduce4(P[r][0], P[r][1], P[r][2], P[r][3]) * scl;
-            if (iq >= 0 && iq < j.n_my && s < j.bnd[r]) lds_sc[(j.slot0 + r) * j.chunk + (s - j.c0)] = out;
+            // the row's keys [c0, bound) as a buffer: lanes past the bound or
+            // outside the job fall outside it and the hardware drops their
+            // stores, so no branch surrounds the store
+            const int nrec = min(max(j.bnd[r] - j.c0, 0), j.chunk) * 4;
+            const __amdgpu_buffer_rsrc_t row =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(a.scores + (int64_t)(j.row0 + r) * a.sstride + j.c0),
+                                                  0, nrec, kBufferFlags);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), row, in_job ? (s - j.c0) * 4 : nrec, 0, 0);
+            if (kHist) {   // every lane adds: 1 for a stored score, else 0 (no branch)
+                const uint32_t d = radix_key(out) >> kDigit1Shift;
+                atomicAdd(lds_cnt + (r * kBins1 + d) * 64 + ((lane + d) & 63),
+                          (in_job && s < j.bnd[r]) ? 1u : 0u);
+            }
         }
     };
     // q = g & 3 must be a compile-time constant (g = i0 + p, i0 a multiple of 4)
@@ -391,11 +419,12 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
 template <bool kHist>
 __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void score_kernel(ScoreArgs a) {
-    // dynamic LDS: [kGroupRows][chunk] f32 scores, then a 64 KB region that
-    // holds q at the start and the first-digit counters at the end
-    extern __shared__ __align__(16) float lds_dyn[];
-    float *lds_sc = lds_dyn;
-    uint32_t *lds_cnt = (uint32_t *)(lds_dyn + kGroupRows * a.chunk);
+    // dynamic LDS: q of up to four rows, the linear term's A operand, and
+    // (when counting) the first-digit counters [row][digit][64]
+    extern __shared__ __align__(16) unsigned char lds_dyn[];
+    unsigned char *lds_q = lds_dyn;
+    bf16_t *t1_lds = (bf16_t *)(lds_dyn + kLdsQ);
+    uint32_t *lds_cnt = (uint32_t *)(lds_dyn + kLdsQ + kLdsT1);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int yb = blockIdx.y * kGroupRows;   // first row of this block of rows
@@ -487,12 +516,11 @@ void score_kernel(ScoreArgs a) {
 #pragma unroll
         for (int c = 0; c < kBlockPieces; ++c) {
             const int ci = threadIdx.x + c * kScoreThreads;
-            *(u32x4_t *)((unsigned char *)lds_cnt + q_lds_off(ci >> 10, (ci >> 4) & 63, ci & 15)) = qt_blk[c];
+            *(u32x4_t *)(lds_q + q_lds_off(ci >> 10, (ci >> 4) & 63, ci & 15)) = qt_blk[c];
         }
         __syncthreads();
     }
 
-    const bool vec4 = (((uintptr_t)a.scores | (uintptr_t)(a.sstride * 4)) & 15) == 0;
     for (int bi = bi_first; bi < kGroupRows; ++bi) {
         int rg, gmax;
         if (bi == bi_first) { rg = rg_first; gmax = gmax_first; }
@@ -506,70 +534,44 @@ void score_kernel(ScoreArgs a) {
         int tid = threadIdx.x;
         asm volatile("" : "+v"(tid));
 
-        // ---- wave roles: the four waves take every fourth 16-key group of
-        // the chunk, each for all of the group's rows
-        const int nrows = rg, part = wave, parts = 4;
+        // ---- wave roles: wave w takes page w of every block of four pages
+        // of the chunk (4 consecutive 16-key groups), for all of the group's
+        // rows
+        const int nrows = rg;
         WaveJob job;
         job.tid = tid;
         job.lane = tid & 63;
         job.c0 = c0;
         job.chunk = a.chunk;
-        job.slot0 = 0;
         job.row0 = r0;
 #pragma unroll
         for (int r = 0; r < kGroupRows; ++r) job.bnd[r] = r < nrows ? __builtin_amdgcn_readlane(v_bnd, bi + r) : 0;
         const int myend = min(c1, max(max(job.bnd[0], job.bnd[1]), max(job.bnd[2], job.bnd[3])));
-        job.g_first = c0 / kKeysPerMfma + part;
-        job.parts = parts;
-        const int g_end = (myend + kKeysPerMfma - 1) / kKeysPerMfma;
-        job.n_my = job.g_first < g_end ? (g_end - job.g_first + parts - 1) / parts : 0;
+        job.gbase = c0 / kKeysPerMfma + 4 * wave;
+        // groups of the chunk below the last bound, counted from the wave's
+        // first: whole blocks of 16 give the wave 4 each, the last partial
+        // block up to 4
+        const int rem = (myend + kKeysPerMfma - 1) / kKeysPerMfma - job.gbase;
+        job.n_my = rem > 0 ? 4 * (rem >> 4) + min(rem & 15, 4) : 0;
         const int v = bi == bi_first ? v_pages_first : load_pages(bi, c1, job.lane);
         job.vpage = (v >= 0 && v < a.num_pages) ? v : -1;
         const bool staged = bi == bi_first && staged_first;
         const int q_slot = staged ? bi : 0;
-
-        switch (nrows) {   // every wave, also one with no groups (q staging)
-        case 4: score_rows<4>(a, job, lds_sc, (unsigned char *)lds_cnt, q_slot, staged, w_blk); break;
-        case 3: score_rows<3>(a, job, lds_sc, (unsigned char *)lds_cnt, q_slot, staged, w_blk); break;
-        case 2: score_rows<2>(a, job, lds_sc, (unsigned char *)lds_cnt, q_slot, staged, w_blk); break;
-        default: score_rows<1>(a, job, lds_sc, (unsigned char *)lds_cnt, q_slot, staged, w_blk); break;
-        }
-
-        // ---- write the chunk's scores (coalesced, 16 bytes per lane when
-        // the score rows allow it) and add the first-digit counts to the row
-        // totals
-        __syncthreads();
-        if (kHist) {   // q is no longer needed: the region becomes the counters
+        if (kHist) {   // the group's counters start at zero (the syncs in score_rows order this)
             u32x4_t *c4 = (u32x4_t *)lds_cnt;
             const uint32_t z = (uint32_t)tid >> 16;   // 0, built here rather than kept live
             for (int i = tid; i < kHistLds / 4; i += kScoreThreads) c4[i] = u32x4_t{z, z, z, z};
-            __syncthreads();
         }
-        for (int r = 0; r < rg; ++r) {
-            // keys of this row in the chunk (none when its bound lies before c0)
-            const int n = max(min(c1, __builtin_amdgcn_readlane(v_bnd, bi + r)) - c0, 0);
-            float *dst = a.scores + (int64_t)(r0 + r) * a.sstride + c0;
-            const float *src = lds_sc + r * a.chunk;
-            uint32_t *cnt = kHist ? lds_cnt + r * kBins1 * 64 : nullptr;
-            auto count = [&](float x) {
-                const uint32_t d = radix_key(x) >> kDigit1Shift;
-                atomicAdd(cnt + d * 64 + ((job.lane + d) & 63), 1u);
-            };
-            int done = 0;
-            if (vec4) {
-                done = n & ~3;
-                for (int jx = 4 * tid; jx < done; jx += 4 * kScoreThreads) {
-                    const f32x4_t x = *(const f32x4_t *)(src + jx);
-                    *(f32x4_t *)(dst + jx) = x;
-                    if (kHist) { count(x[0]); count(x[1]); count(x[2]); count(x[3]); }
-                }
-            }
-            for (int jx = done + tid; jx < n; jx += kScoreThreads) {
-                const float x = src[jx];
-                dst[jx] = x;
-                if (kHist) count(x);
-            }
+
+        switch (nrows) {   // every wave, also one with no groups (q staging)
+        case 4: score_rows<4, kHist>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, w_blk); break;
+        case 3: score_rows<3, kHist>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, w_blk); break;
+        case 2: score_rows<2, kHist>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, w_blk); break;
+        default: score_rows<1, kHist>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, w_blk); break;
         }
+
+        // ---- add the chunk's first-digit counts to the row totals: wave r
+        // sums row r's counters (lane = digit) into copy (workgroup % 16)
         if (kHist) {
             __syncthreads();
             const int hr = tid >> 6;   // row slot; lane = digit
@@ -588,7 +590,7 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t st) {
     if (a.max_bound <= 0) return hipSuccess;
     const int nchunks = (a.max_bound + a.chunk - 1) / a.chunk;
     dim3 grid(nchunks, (a.rows + kGroupRows - 1) / kGroupRows);
-    const size_t lds = (size_t)kGroupRows * a.chunk * sizeof(float) + kHistLds * sizeof(uint32_t);
+    const size_t lds = (size_t)kLdsQ + kLdsT1 + (a.hist1 ? kLdsCnt : 0);
     if (a.hist1)
         hipLaunchKernelGGL(score_kernel<true>, grid, dim3(kScoreThreads), lds, st, a);
     else
