@@ -45,6 +45,27 @@ __global__ __launch_bounds__(256) void mfma_kernel(const bf16x8_t *in, float *ou
     if (s == 1234.5f) out[blockIdx.x] = s;
 }
 
+// The same with v_mfma_f32_32x32x16_bf16 (twice the work per instruction):
+// four independent accumulators per wave.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+__global__ __launch_bounds__(256) void mfma32_kernel(const bf16x8_t *in, float *out, int iters) {
+    const int lane = threadIdx.x & 63;
+    bf16x8_t a[4], b[2];
+    for (int i = 0; i < 4; ++i) a[i] = in[lane * 6 + i];
+    for (int i = 0; i < 2; ++i) b[i] = in[lane * 6 + 4 + i];
+    f32x16_t acc[4];
+    for (int i = 0; i < 4; ++i) acc[i] = f32x16_t{};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m & 3], b[(m >> 2) & 1], acc[m & 3], 0, 0, 0);
+    }
+    float s = 0.f;
+    for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 16; ++j) s += acc[i][j];
+    if (s == 1234.5f) out[blockIdx.x] = s;
+}
+
 extern "C" {
 
 // Reads `bytes` (a multiple of 16) from device memory at `src` once.
@@ -60,6 +81,15 @@ int peak_read(const void *src, size_t bytes, uint32_t *out, int blocks, void *st
 int peak_mfma(const void *in, float *out, int iters, int blocks, void *stream) {
     if (!in || !out || iters < 1 || blocks < 1) return -1;
     hipLaunchKernelGGL(mfma_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       (const bf16x8_t *)in, out, iters);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+// `blocks` workgroups of 4 waves, each wave `iters` x 8 MFMAs of 32x32x16
+// (the same flops per wave and iteration as peak_mfma).
+int peak_mfma32(const void *in, float *out, int iters, int blocks, void *stream) {
+    if (!in || !out || iters < 1 || blocks < 1) return -1;
+    hipLaunchKernelGGL(mfma32_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
                        (const bf16x8_t *)in, out, iters);
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
