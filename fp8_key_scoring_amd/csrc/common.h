@@ -45,6 +45,10 @@ constexpr int kBins3 = 1 << kDigit3Bits;                     // 256
 // and hundreds of workgroups adding into one word would queue behind each
 // other.  Readers sum the copies.
 constexpr int kHist1Slots = 16;
+// The same for the second-digit counts: the 64 refine workgroups of a row add
+// ~a hundred bins each into the row's 256, and each bin would take one atomic
+// per workgroup in turn; workgroup x adds into copy x % kHist2Slots.
+constexpr int kHist2Slots = 8;
 
 // Per-row selection state: b1 and above1 written by the first refine
 // workgroup of a row, the rest by the first gather workgroup.
@@ -66,7 +70,7 @@ struct RowState {
 // it reads.
 struct WsLayout {
     size_t hist1;      // u32 [rz][kHist1Slots][64]  first-digit counts
-    size_t hist2;      // u32 [rz][256]     second-digit counts inside the first-digit bin
+    size_t hist2;      // u32 [rz][kHist2Slots][256]  second-digit counts inside the first-digit bin
     size_t hist3;      // u32 [rz][256]     third-digit counts of the candidates
     size_t state;      // RowState [rows]
     size_t ent_cnt;    // u32 [rows][sel_wgs]              entries (sure keys + candidates) per gather workgroup
@@ -95,7 +99,7 @@ inline WsLayout ws_layout(int rows, int max_bound, bool own_scores) {
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
     const size_t rz = (size_t)(rows > kZeroRows ? rows : kZeroRows);
     L.hist1 = take(rz * kHist1Slots * kBins1 * 4);
-    L.hist2 = take(rz * kBins2 * 4);
+    L.hist2 = take(rz * kHist2Slots * kBins2 * 4);
     L.hist3 = take(rz * kBins3 * 4);
     L.state = take((size_t)rows * sizeof(RowState));
     L.ent_cnt = take((size_t)rows * n * 4);

@@ -19,7 +19,7 @@
 // back the whole L2 of an XCD, which costs far more than a dependent launch):
 //   hist1    (only for indexer_topk) first-digit counts of stored scores;
 //   refine   second-digit counts inside the first-digit bin, added to the
-//            row's histogram with one atomic per non-empty bin per workgroup
+//            row's histogram (copy x % kHist2Slots for workgroup x) with one atomic per non-empty bin
 //            (the first workgroup also records the first-digit bin);
 //   gather   every workgroup derives the same split from that bin and the
 //            second-digit histogram, writes its sure keys and candidates as
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kSelThreads) void refine_kernel(SelectArgs a) {
     if (t < kBins2) {
         uint32_t c = 0;
         for (int w = 0; w < kWaves; ++w) c += h2[w][t];
-        if (c) atomicAdd((uint32_t *)(a.ws + a.L.hist2) + (int64_t)r * kBins2 + t, c);
+        if (c) atomicAdd((uint32_t *)(a.ws + a.L.hist2) + ((int64_t)r * kHist2Slots + x % kHist2Slots) * kBins2 + t, c);
     }
 }
 
@@ -274,12 +274,18 @@ __global__ __launch_bounds__(kSelThreads) void gather_kernel(SelectArgs a) {
     // sits behind a branch and the waits stay exact.
     const RowState *st_in = (const RowState *)(a.ws + a.L.state) + r;
     const uint32_t b1 = st_in->b1, above1 = st_in->above1;
-    const uint32_t c2 = ((const uint32_t *)(a.ws + a.L.hist2))[(int64_t)r * kBins2 + (t & (kBins2 - 1))];
+    uint32_t c2s[kHist2Slots];   // the row's second-digit counts: the sum of its copies
+#pragma unroll
+    for (int sl = 0; sl < kHist2Slots; ++sl)
+        c2s[sl] = ((const uint32_t *)(a.ws + a.L.hist2))[((int64_t)r * kHist2Slots + sl) * kBins2 + (t & (kBins2 - 1))];
     __builtin_amdgcn_sched_barrier(0);
     float v0[kSelUnroll];
     load_raw(row, s0, s1, v0);   // (b > k >= 1, so key s1 - 1 exists also when s0 >= s1)
     __builtin_amdgcn_sched_barrier(0);
     if (t < kBins2) {
+        uint32_t c2 = 0;
+#pragma unroll
+        for (int sl = 0; sl < kHist2Slots; ++sl) c2 += c2s[sl];
         h2[t] = c2;
         h3[t] = 0;
     }
@@ -555,7 +561,8 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
         }
     }
     if (t < kHist1Slots * kBins1) ((uint32_t *)(a.ws + a.L.hist1))[(int64_t)r * kHist1Slots * kBins1 + t] = 0;
-    if (t < kBins2) ((uint32_t *)(a.ws + a.L.hist2))[(int64_t)r * kBins2 + t] = 0;
+    for (int i = t; i < kHist2Slots * kBins2; i += kSelThreads)
+        ((uint32_t *)(a.ws + a.L.hist2))[(int64_t)r * kHist2Slots * kBins2 + i] = 0;
     if (t < kBins3) hist3[t] = 0;
 }
 
