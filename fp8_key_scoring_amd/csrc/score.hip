@@ -70,11 +70,14 @@ constexpr int kBlockPieces = kGroupRows * kHeads * kDim / 8 / kScoreThreads;   /
 // Word 3 of a raw buffer resource for 32-bit accesses (32-bit data format).
 constexpr int kBufferFlags = 0x00020000;
 
-// Dynamic LDS: q of four rows, then the linear term's A operand, then (when
-// counting) the first-digit counters.
+// Dynamic LDS: q of four rows, then the linear term's A operand.  q is read
+// only while a row group is set up; when counting, the same 64 KB then hold
+// the first-digit counters.  (A launch asking for twice the LDS, q and the
+// counters side by side, costs about 3 us more to start even when its
+// workgroups return at once.)
 constexpr int kLdsQ = kGroupRows * kHeads * kDim * 2;     // 64 KB
 constexpr int kLdsT1 = 4 * 64 * 8 * 2;                   // [ks][lane][8] bf16, 4 KB
-constexpr int kLdsCnt = kHistLds * 4;                    // 64 KB
+static_assert(kHistLds * 4 == kLdsQ, "the counters reuse the q region");
 
 // The same pointer, held in scalar registers and opaque to the optimiser:
 // a load from it plus a 32-bit lane offset then uses the scalar-base
@@ -266,6 +269,12 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
             t1a[ks] = t1_row ? v : bf16x8_t{};
         }
         __syncthreads();   // t1_lds may be written again by the next row group
+        if (kHist) {   // every wave is done with q in LDS: the region becomes the counters
+            u32x4_t *c4 = (u32x4_t *)lds_cnt;
+            const uint32_t z = (uint32_t)tid >> 16;   // 0, built here rather than kept live
+            for (int i = tid; i < kHistLds / 4; i += kScoreThreads) c4[i] = u32x4_t{z, z, z, z};
+            __syncthreads();
+        }
     }
     if (j.n_my == 0) return;
     // q lives in AGPRs: the MFMA reads its A operand from there directly,
@@ -419,12 +428,12 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
 template <bool kHist>
 __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void score_kernel(ScoreArgs a) {
-    // dynamic LDS: q of up to four rows, the linear term's A operand, and
-    // (when counting) the first-digit counters [row][digit][64]
+    // dynamic LDS: q of up to four rows (when counting, then the first-digit
+    // counters [row][digit][64]) and the linear term's A operand
     extern __shared__ __align__(16) unsigned char lds_dyn[];
     unsigned char *lds_q = lds_dyn;
     bf16_t *t1_lds = (bf16_t *)(lds_dyn + kLdsQ);
-    uint32_t *lds_cnt = (uint32_t *)(lds_dyn + kLdsQ + kLdsT1);
+    uint32_t *lds_cnt = (uint32_t *)lds_dyn;   // the q region, once q is in registers
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int yb = blockIdx.y * kGroupRows;   // first row of this block of rows
@@ -557,12 +566,6 @@ void score_kernel(ScoreArgs a) {
         job.vpage = (v >= 0 && v < a.num_pages) ? v : -1;
         const bool staged = bi == bi_first && staged_first;
         const int q_slot = staged ? bi : 0;
-        if (kHist) {   // the group's counters start at zero (the syncs in score_rows order this)
-            u32x4_t *c4 = (u32x4_t *)lds_cnt;
-            const uint32_t z = (uint32_t)tid >> 16;   // 0, built here rather than kept live
-            for (int i = tid; i < kHistLds / 4; i += kScoreThreads) c4[i] = u32x4_t{z, z, z, z};
-        }
-
         switch (nrows) {   // every wave, also one with no groups (q staging)
         case 4: score_rows<4, kHist>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, w_blk); break;
         case 3: score_rows<3, kHist>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, w_blk); break;
@@ -590,7 +593,7 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t st) {
     if (a.max_bound <= 0) return hipSuccess;
     const int nchunks = (a.max_bound + a.chunk - 1) / a.chunk;
     dim3 grid(nchunks, (a.rows + kGroupRows - 1) / kGroupRows);
-    const size_t lds = (size_t)kLdsQ + kLdsT1 + (a.hist1 ? kLdsCnt : 0);
+    const size_t lds = (size_t)kLdsQ + kLdsT1;
     if (a.hist1)
         hipLaunchKernelGGL(score_kernel<true>, grid, dim3(kScoreThreads), lds, st, a);
     else
