@@ -262,22 +262,25 @@ __global__ __launch_bounds__(kSelThreads) void gather_kernel(SelectArgs a) {
             for (int i = t; i < k; i += kSelThreads) out_row[i] = i < b ? i : -1;
         return;
     }
+    const int64_t s0 = (int64_t)x * a.L.sel_chunk;
+    if (s0 >= b) return;   // past the row's bound: finalize counts this slice as empty
     unsigned long long *slice_e = (unsigned long long *)(a.ws + a.L.ent_list) + ((int64_t)r * S + x) * kSliceCap;
     const float *row = a.scores + (int64_t)r * a.sstride;
-    const int64_t s0 = (int64_t)x * a.L.sel_chunk;
     const int64_t s1 = min(s0 + a.L.sel_chunk, (int64_t)b);
 
     // ---- the split: (b1, above1) as refine found them, (b2, above2) from
     // the second digit.  The state and counts are loaded before the first
     // step's keys (loads complete in order), so the split waits on them
-    // alone and the key loads overlap it.  Every thread loads, so no load
-    // sits behind a branch and the waits stay exact.
+    // alone and the key loads overlap it.  The count copies are loaded by
+    // the four waves that sum them (a wave-uniform condition).
     const RowState *st_in = (const RowState *)(a.ws + a.L.state) + r;
     const uint32_t b1 = st_in->b1, above1 = st_in->above1;
-    uint32_t c2s[kHist2Slots];   // the row's second-digit counts: the sum of its copies
+    uint32_t c2s[kHist2Slots] = {};   // the row's second-digit counts: the sum of its copies
+    if (t < kBins2) {                  // (waves 0-3: a wave-uniform branch)
 #pragma unroll
-    for (int sl = 0; sl < kHist2Slots; ++sl)
-        c2s[sl] = ((const uint32_t *)(a.ws + a.L.hist2))[((int64_t)r * kHist2Slots + sl) * kBins2 + (t & (kBins2 - 1))];
+        for (int sl = 0; sl < kHist2Slots; ++sl)
+            c2s[sl] = ((const uint32_t *)(a.ws + a.L.hist2))[((int64_t)r * kHist2Slots + sl) * kBins2 + t];
+    }
     __builtin_amdgcn_sched_barrier(0);
     float v0[kSelUnroll];
     load_raw(row, s0, s1, v0);   // (b > k >= 1, so key s1 - 1 exists also when s0 >= s1)
@@ -437,6 +440,7 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
     __shared__ unsigned long long ent[kEntCap];   // the row's entries, ascending index
     __shared__ unsigned long long tie[kTieCap];   // candidates inside the third-digit bin
     __shared__ uint32_t offe[kSelMaxWgs + 1];
+    __shared__ uint32_t roff[kSelMaxWgs + 1];    // exclusive prefix of the entries past 16*kPre per slice
     __shared__ uint32_t h3[kBins3];
     __shared__ uint32_t wsum[kWaves], wtie[kWaves];
     __shared__ int sB;
@@ -463,6 +467,8 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
         const int xs = x < S ? x : 0;
         const RowState st = ((const RowState *)(a.ws + a.L.state))[r];
         const uint32_t h3v = hist3[t & (kBins3 - 1)];
+        // slices that start at or past the bound were not written: empty
+        const bool live = lane < S && (int64_t)lane * a.L.sel_chunk < b;
         const uint32_t ne = ecnt[lane < S ? lane : 0], ncx = ccnt[lane < S ? lane : 0];
         unsigned long long pre[kPre];
 #pragma unroll
@@ -473,16 +479,19 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
         // slice offsets (exclusive prefix of the entry counts); candidates
         // past a slice's capacity or the row's send the row to the fallback
         if (wave == 0) {
-            const uint32_t c = lane < S ? ne : 0u, cc = lane < S ? ncx : 0u;
+            const uint32_t c = live ? ne : 0u, cc = live ? ncx : 0u;
+            const uint32_t rm = c > 16u * kPre ? c - 16u * kPre : 0u;
             const uint64_t big = __ballot(cc > (uint32_t)kCandSlice);
-            uint32_t incl = c, cincl = cc;
+            uint32_t incl = c, cincl = cc, rincl = rm;
             for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t v = __shfl_up(incl, o), w = __shfl_up(cincl, o);
-                if (lane >= o) { incl += v; cincl += w; }
+                const uint32_t v = __shfl_up(incl, o), w = __shfl_up(cincl, o), z = __shfl_up(rincl, o);
+                if (lane >= o) { incl += v; cincl += w; rincl += z; }
             }
             offe[lane] = incl - c;
+            roff[lane] = rincl - rm;
             if (lane == 63) {
                 offe[kSelMaxWgs] = incl;
+                roff[kSelMaxWgs] = rincl;
                 ovf = (big != 0ull) || cincl > (uint32_t)kCandCap || incl > (uint32_t)kEntCap;
             }
         }
@@ -498,7 +507,33 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
 #pragma unroll
                 for (int m = 0; m < kPre; ++m)
                     if (j0 + 16 * m < n) ent[o + j0 + 16 * m] = pre[m];
-                for (int jj = j0 + 16 * kPre; jj < n; jj += 16) ent[o + jj] = sl[(int64_t)x * kSliceCap + jj];
+            }
+            // entries past the first 16*kPre of their slice (a short row puts
+            // all its entries in one or two slices): spread over every thread,
+            // each finding its slice by a binary search of roff; all loads go
+            // out before any is stored
+            const int NR = (int)roff[kSelMaxWgs];
+            if (NR > 0) {
+                int dst[kPer];
+                unsigned long long v[kPer];
+#pragma unroll
+                for (int m = 0; m < kPer; ++m) {
+                    const int i = m * kSelThreads + t;
+                    dst[m] = -1;
+                    if (i < NR) {
+                        int lo = 0, hi = S - 1;   // the last slice with roff <= i
+                        while (lo < hi) {
+                            const int mid = (lo + hi + 1) >> 1;
+                            if ((int)roff[mid] <= i) lo = mid; else hi = mid - 1;
+                        }
+                        const int jj = 16 * kPre + (i - (int)roff[lo]);
+                        dst[m] = (int)offe[lo] + jj;
+                        v[m] = sl[(int64_t)lo * kSliceCap + jj];
+                    }
+                }
+#pragma unroll
+                for (int m = 0; m < kPer; ++m)
+                    if (dst[m] >= 0) ent[dst[m]] = v[m];
             }
             if (t < 64) wave_find_bin(h3, kBins3 / 64, (uint32_t)need, lane, &sB, &sAbove);
             __syncthreads();
