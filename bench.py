@@ -217,13 +217,24 @@ def main():
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    # the K timed steps, split into up to 7 trials by events recorded between
+    # them on the launch stream (an event adds no gap); the value is the whole
+    # block, the trials give the spread
+    n_trials = max(1, min(7, args.steps))
+    bounds = [args.steps * t // n_trials for t in range(n_trials + 1)]
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(n_trials + 1)]
     e0.record(stream)
-    for i in range(args.steps):
-        step(i)
+    marks[0].record(stream)
+    for t in range(n_trials):
+        for i in range(bounds[t], bounds[t + 1]):
+            step(i)
+        marks[t + 1].record(stream)
     e1.record(stream)
     torch.cuda.synchronize()
     ms_total = e0.elapsed_time(e1)
     ms_step = ms_total / args.steps
+    trial_us = sorted(marks[t].elapsed_time(marks[t + 1]) * 1e3 / (bounds[t + 1] - bounds[t])
+                      for t in range(n_trials))
 
     # hot variant: one pool (keys may stay in the MALL between launches)
     for i in range(args.warmup):
@@ -283,6 +294,8 @@ def main():
         "ms_per_step": ms_step,
         "us_per_launch": ms_step * 1e3,
         "us_per_launch_hot": ms_step_hot * 1e3,
+        "us_per_launch_trials": {"n": n_trials, "median": round(trial_us[n_trials // 2], 2),
+                                 "min": round(trial_us[0], 2), "max": round(trial_us[-1], 2)},
         "launch_roofline_frac": round(step_roof_s / (ms_step * 1e-3), 4),
         "higher_is_better": True,
         "scaling": "weak",
