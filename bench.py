@@ -34,7 +34,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--pools", type=int, default=4, help="key-pool copies rotated over")
-    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (3 = 512K keys x 4 rows)")
+    ap.add_argument("--config", type=int, default=3, help="workload 1..7 (3 = 512K keys x 4 rows)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",

@@ -236,7 +236,10 @@ def verify_rows(req: int, n: int, count: int = 4) -> List[Tuple[int, int]]:
 # the five workloads
 # --------------------------------------------------------------------------
 CONFIG_NAMES = ["c1_1row_8k", "c2_4rows_128k", "c3_4rows_512k", "c4_8rows_512k_384k",
-                "c5_256rows_loguniform"]
+                "c5_256rows_loguniform",
+                # small-row groups over a long context (HBM-bound): one row, and
+                # two verify rows, of one 524,288-key request
+                "c6_1row_512k", "c7_2rows_512k"]
 
 
 def c5_lengths(rng: np.random.Generator, nreq: int = 64,
@@ -246,7 +249,7 @@ def c5_lengths(rng: np.random.Generator, nreq: int = 64,
 
 
 def make_config(idx: int) -> Problem:
-    """Workload idx in 1..5 (seed 1000 + idx)."""
+    """Workload idx in 1..7 (seed 1000 + idx)."""
     seed = 1000 + idx
     if idx == 1:
         return build_problem(CONFIG_NAMES[0], seed, [8192], [(0, 8192)])
@@ -267,6 +270,12 @@ def make_config(idx: int) -> Problem:
         for i, n in enumerate(lens):
             rows += verify_rows(i, n)
         return build_problem(CONFIG_NAMES[4], seed + 10_000, lens, rows)
+    if idx == 6:
+        n = 524288
+        return build_problem(CONFIG_NAMES[5], seed, [n], [(0, n)])
+    if idx == 7:
+        n = 524288
+        return build_problem(CONFIG_NAMES[6], seed, [n], verify_rows(0, n, 2))
     raise ValueError(idx)
 
 

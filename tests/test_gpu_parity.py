@@ -146,3 +146,13 @@ def test_c4_two_requests_8_rows():
 
 def test_c5_batch_256_rows():
     _big(5, overlap_rows=[0, 1, 2, 3, 100, 101, 254, 255])
+
+
+def test_c6_one_row_512k():
+    # a lone row over a long context: every wave scores one row (HBM-bound)
+    _big(6)
+
+
+def test_c7_two_rows_512k():
+    # a two-row group over a long context
+    _big(7)
