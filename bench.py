@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--config", type=int, default=3, help="workload 1..7 (3 = 512K keys x 4 rows)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--shards", type=int, default=0,
+                    help="time the key-sharded selection instead: one shard's launch, its "
+                         "candidates and the merge of G shards (G GPUs emulated on one)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -181,6 +184,65 @@ def measured_peaks(torch, dev):
                    "accumulators and random operands (the better form is the measured peak)"}
 
 
+def sharded_report(args):
+    """Key-sharded selection with G = args.shards shards (pages interleaved):
+    the time one shard's launch takes (what each of G GPUs would spend), the
+    conversion of its selection to (score, global index) candidates, and the
+    merge of all G shards' candidates (run once, after the exchange).  Each
+    part is timed over back-to-back calls between events on the launch
+    stream."""
+    import torch
+    import fp8_key_scoring_amd as fk
+    import synthetic as syn
+    fk.load_library()
+    dev = "cuda:0"
+    G = args.shards
+    p = syn.make_config(args.config)
+    k = p.topk
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n):
+        for i in range(min(5, n)):
+            fn(i)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    cand_s = torch.empty((p.rows, G * k), dtype=torch.float32, device=dev)
+    cand_i = torch.empty((p.rows, G * k), dtype=torch.int32, device=dev)
+    shard_us, cand_us = [], []
+    for g in range(G):
+        ps = syn.shard_problem(p, g, G)
+        d = syn.device_arrays(ps, dev)
+        mb = ps.max_bound
+        scores = torch.empty((ps.rows, max(1, mb)), dtype=torch.float32, device=dev)
+        out = torch.empty((ps.rows, k), dtype=torch.int32, device=dev)
+        prob = fk._problem_from(d["q"], d["k_e4m3"], d["page_table"], mb, k, scores.stride(0))
+        ws = fk.new_workspace(prob, False, dev)
+        shard_us.append(timed(lambda i: fk.indexer_launch(**d, max_bound=mb, topk=k, scores=scores,
+                                                          out_idx=out, workspace=ws), args.steps))
+        cand_us.append(timed(lambda i: fk.indexer_shard_candidates(scores, out, shard=g, shards=G, max_bound=mb,
+                                                                   cand_score=cand_s, cand_idx=cand_i),
+                             args.steps))
+    merged = torch.empty((p.rows, k), dtype=torch.int32, device=dev)
+    merge_us = timed(lambda i: fk.indexer_merge_topk(cand_s, cand_i, shards=G, topk=k, out_idx=merged),
+                     args.steps)
+    print(json.dumps({"metric": "key-sharded selection: per-shard launch, candidates and merge µs",
+                      "config": {"workload": p.name, "shards": G, "rows": p.rows, "topk": k},
+                      "shard_launch_us": {"median": round(float(np.median(shard_us)), 2),
+                                          "max": round(max(shard_us), 2)},
+                      "candidates_us": round(float(np.median(cand_us)), 2),
+                      "merge_us": round(merge_us, 2),
+                      "merge_bytes": p.rows * G * k * 8 + p.rows * k * 4,
+                      "steps": args.steps}))
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -189,6 +251,9 @@ def main():
         sys.exit(2)
     if args.copy_calib:
         copy_calib()
+        return
+    if args.shards > 0:
+        sharded_report(args)
         return
     import torch
     import fp8_key_scoring_amd as fk

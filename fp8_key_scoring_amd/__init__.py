@@ -21,7 +21,8 @@ PAGE = 64
 MAX_TOPK = 2048
 
 EXPORTED = ("fp8idx_abi_version", "fp8idx_strerror", "fp8idx_workspace_size",
-            "fp8idx_workspace_init", "indexer_score", "indexer_topk", "indexer_launch")
+            "fp8idx_workspace_init", "indexer_score", "indexer_topk", "indexer_launch",
+            "indexer_shard_candidates", "indexer_merge_topk")
 
 
 class Problem(ctypes.Structure):
@@ -70,6 +71,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.indexer_launch.restype = ctypes.c_int
     lib.indexer_launch.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, P, P,
                                    ctypes.c_size_t, P]
+    lib.indexer_shard_candidates.restype = ctypes.c_int
+    lib.indexer_shard_candidates.argtypes = [ctypes.POINTER(Problem), ctypes.c_int, ctypes.c_int,
+                                             P, P, P, P, P]
+    lib.indexer_merge_topk.restype = ctypes.c_int
+    lib.indexer_merge_topk.argtypes = [ctypes.POINTER(Problem), ctypes.c_int, P, P, P, P]
     _lib = lib
     return lib
 
@@ -184,4 +190,44 @@ def indexer_launch(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound, *, max_
                                          _ptr(k_scale), _ptr(page_table), _ptr(row_pt),
                                          _ptr(row_bound), _ptr(scores), _ptr(out_idx),
                                          _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return out_idx
+
+
+def indexer_shard_candidates(scores, out_idx, *, shard: int, shards: int, max_bound: int,
+                             cand_score=None, cand_idx=None):
+    """Shard `shard` of `shards` (pages interleaved): its selection out_idx
+    [rows, topk] (logical indices) and scores [rows, stride] become (score,
+    global index) candidates in block `shard` of cand_score / cand_idx
+    [rows, shards * topk]."""
+    import torch
+    R, k = out_idx.shape
+    assert scores.dtype == torch.float32 and scores.dim() == 2 and scores.stride(1) == 1
+    assert out_idx.dtype == torch.int32 and out_idx.is_contiguous()
+    if cand_score is None:
+        cand_score = torch.empty((R, shards * k), dtype=torch.float32, device=scores.device)
+    if cand_idx is None:
+        cand_idx = torch.empty((R, shards * k), dtype=torch.int32, device=scores.device)
+    assert cand_score.is_contiguous() and cand_idx.is_contiguous()
+    prob = make_problem(rows=R, num_pages=1, pt_rows=1, pt_stride=max(1, (max_bound + 63) // 64),
+                        max_bound=max_bound, topk=k, score_stride=scores.stride(0))
+    _check(load_library().indexer_shard_candidates(ctypes.byref(prob), shard, shards, _ptr(scores),
+                                                   _ptr(out_idx), _ptr(cand_score), _ptr(cand_idx),
+                                                   _stream(scores.device)))
+    return cand_score, cand_idx
+
+
+def indexer_merge_topk(cand_score, cand_idx, *, shards: int, topk: int = MAX_TOPK, out_idx=None):
+    """Exact top-k per row of the shards' candidates: global indices grouped
+    by shard (each group ascending), -1 padded.  Returns out_idx [rows, topk]
+    int32."""
+    import torch
+    R = cand_idx.shape[0]
+    assert cand_score.dtype == torch.float32 and cand_idx.dtype == torch.int32
+    assert cand_score.is_contiguous() and cand_idx.is_contiguous()
+    assert cand_idx.numel() == R * shards * topk and cand_score.numel() == R * shards * topk
+    if out_idx is None:
+        out_idx = torch.empty((R, topk), dtype=torch.int32, device=cand_idx.device)
+    prob = make_problem(rows=R, num_pages=1, pt_rows=1, pt_stride=1, max_bound=0, topk=topk)
+    _check(load_library().indexer_merge_topk(ctypes.byref(prob), shards, _ptr(cand_score), _ptr(cand_idx),
+                                             _ptr(out_idx), _stream(cand_idx.device)))
     return out_idx

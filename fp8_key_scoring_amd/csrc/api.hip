@@ -195,4 +195,42 @@ int indexer_launch(const fp8idx_problem_t *p, const void *q_bf16, const float *w
     return run_select(p, sc, sstride, row_bound, out_idx, wsb, L, false, st);
 }
 
+static int check_shards(const fp8idx_problem_t *p, int shards) {
+    if (shards < 1 || (int64_t)shards * p->topk > kMergeMaxCand) return FP8IDX_EINVAL;
+    if ((int64_t)shards * ((int64_t)p->max_bound + FP8IDX_PAGE) >= ((int64_t)1 << 31)) return FP8IDX_EINVAL;
+    return FP8IDX_OK;
+}
+
+int indexer_shard_candidates(const fp8idx_problem_t *p, int shard, int shards,
+                             const float *scores, const int32_t *out_idx,
+                             float *cand_score, int32_t *cand_idx, void *stream) {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if ((rc = check_shards(p, shards))) return rc;
+    if (shard < 0 || shard >= shards) return FP8IDX_EINVAL;
+    if (!scores || !out_idx || !cand_score || !cand_idx) return FP8IDX_EINVAL;
+    if (!aligned(scores, 4) || !aligned(out_idx, 4) || !aligned(cand_score, 4) || !aligned(cand_idx, 4))
+        return FP8IDX_EINVAL;
+    if (p->score_stride < p->max_bound) return FP8IDX_EINVAL;
+    rc = check_device();
+    if (rc) return rc;
+    return to_code(launch_shard_cand(scores, p->score_stride, out_idx, p->rows, p->topk, shard, shards,
+                                     cand_score, cand_idx, (hipStream_t)stream));
+}
+
+int indexer_merge_topk(const fp8idx_problem_t *p, int shards,
+                       const float *cand_score, const int32_t *cand_idx,
+                       int32_t *out_idx, void *stream) {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if ((rc = check_shards(p, shards))) return rc;
+    if (!cand_score || !cand_idx || !out_idx) return FP8IDX_EINVAL;
+    if (!aligned(cand_score, 16) || !aligned(cand_idx, 16) || !aligned(out_idx, 4)) return FP8IDX_EINVAL;
+    if ((shards * p->topk) % 16) return FP8IDX_EINVAL;
+    rc = check_device();
+    if (rc) return rc;
+    return to_code(launch_merge(p->rows, shards * p->topk, p->topk, cand_score, cand_idx, out_idx,
+                                (hipStream_t)stream));
+}
+
 }  // extern "C"

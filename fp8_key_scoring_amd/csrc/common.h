@@ -149,5 +149,10 @@ hipError_t launch_refine(const SelectArgs &a, hipStream_t st);
 hipError_t launch_gather(const SelectArgs &a, hipStream_t st);
 hipError_t launch_finalize(const SelectArgs &a, hipStream_t st);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
+hipError_t launch_shard_cand(const float *scores, int64_t sstride, const int32_t *out_idx, int rows, int k,
+                             int g, int G, float *cand_score, int32_t *cand_idx, hipStream_t st);
+hipError_t launch_merge(int rows, int n, int k, const float *cand_score, const int32_t *cand_idx,
+                        int32_t *out_idx, hipStream_t st);
+constexpr int kMergeMaxCand = 16384;   // shards * topk the merge holds per row
 
 }  // namespace fp8idx

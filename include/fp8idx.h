@@ -144,6 +144,39 @@ int indexer_launch(const fp8idx_problem_t *p,
                    float *scores, int32_t *out_idx,
                    void *ws, size_t ws_bytes, void *stream);
 
+/* ---- Key-sharded selection (the context split over G shards by page).
+ * Shard g of G (0 <= g < G) holds pages g, g+G, g+2G, ... of every request
+ * in its own page table and runs indexer_launch (with `scores`) on them; its
+ * logical key s is global key 64 * (g + G * (s / 64)) + s % 64 (the release
+ * test-suite page for GLM-5.2: 64-key pages interleaved over ranks, a
+ * top-k owner merge).  Every key scores the same in any shard, so the exact
+ * top-k of the union of the shards' top-k sets is the row's global top-k. */
+
+/* Step 1, per shard: turns shard g's selection out_idx [rows][topk] (its
+ * logical indices, -1 padded) and its scores [rows][score_stride] into
+ * (score, global index) candidates at cand_score / cand_idx
+ * [rows][shards][topk], block g; empty slots get index -1.  Uses p->rows,
+ * max_bound, topk, score_stride of the shard's problem.  Errors: -1 for a
+ * null or misaligned pointer, shard outside [0, shards), shards * topk above
+ * 16384, or global indices that would not fit in int32
+ * (shards * (max_bound + 64) >= 2^31).  No workspace. */
+int indexer_shard_candidates(const fp8idx_problem_t *p, int shard, int shards,
+                             const float *scores, const int32_t *out_idx,
+                             float *cand_score, int32_t *cand_idx, void *stream);
+
+/* Step 2, once the candidates of all shards are in one place: out_idx
+ * [rows][topk] receives each row's exact top-topk of its shards * topk
+ * candidates (descending score, equal scores to the lower global index, NaN
+ * below every number) as global indices in candidate-slot order (grouped by
+ * shard, shard 0 first; ascending within a shard for the candidates step 1
+ * writes), -1 padded when fewer than topk candidates exist.  Uses p->rows and
+ * p->topk.  cand_score and cand_idx must be 16-byte aligned and shards * topk
+ * a multiple of 16.  Errors as for step 1 (-1 also for those).  No
+ * workspace. */
+int indexer_merge_topk(const fp8idx_problem_t *p, int shards,
+                       const float *cand_score, const int32_t *cand_idx,
+                       int32_t *out_idx, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -125,3 +125,25 @@ def topk(scores: np.ndarray, k: int) -> np.ndarray:
     if rc != 0:
         raise RuntimeError(f"oracle_topk failed: {rc}")
     return out
+
+
+def merge_topk(cand_scores: np.ndarray, cand_idx: np.ndarray, k: int) -> np.ndarray:
+    """Exact top-k of one row over candidate (score, global index) pairs, the
+    union of the shards' own top-k sets when the context is split over shards
+    by page (the GLM-5.2 release test-suite page: 64-key pages interleaved
+    over ranks, top-k merged by owner).  Order as for the unsharded top-k:
+    larger score first, NaN below every number, equal scores (and -0 == +0)
+    to the lower global index.  Candidates with index -1 are empty.  Returns
+    the selected global indices ascending, int32[k] padded with -1.
+
+    The plain definition, written out: a stable sort of the valid pairs by
+    (-score, index), the first k."""
+    s = np.asarray(cand_scores, dtype=np.float32).ravel()
+    i = np.asarray(cand_idx, dtype=np.int64).ravel()
+    keep = i >= 0
+    s, i = s[keep], i[keep]
+    order = np.lexsort((i, -s.astype(np.float64)))   # NaN sorts last in either sign
+    sel = np.sort(i[order[:k]])
+    out = np.full(k, -1, dtype=np.int32)
+    out[:sel.size] = sel
+    return out

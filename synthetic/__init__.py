@@ -313,6 +313,30 @@ def scale_tie_problem(n: int = 12000, topk: int = TOPK, seed: int = 7,
                    row_bound=np.array([n], np.int32), topk=topk, seed=seed)
 
 
+def shard_problem(p: Problem, g: int, shards: int) -> Problem:
+    """Shard g of `shards` of a problem split by page: the shard holds pages
+    g, g+shards, g+2*shards, ... of every request (the same pool; its page
+    table lists them in that order), so its logical key s is the request's key
+    64 * (g + shards * (s // 64)) + s % 64.  Row bounds become the number of
+    the shard's keys below the row's bound."""
+    pt = np.asarray(p.page_table)
+    stride = pt.shape[1]
+    sub = pt[:, g::shards]
+    if sub.shape[1] == 0:
+        sub = np.full((pt.shape[0], 1), -1, dtype=np.int32)
+    bounds = []
+    for r in range(p.rows):
+        b = int(p.row_bound[r])
+        full, rem = divmod(b, PAGE)              # whole pages below the bound, keys of the next
+        nfull = max(0, -(-(full - g) // shards)) if full > g else 0   # shard pages among them
+        part = rem if (rem and full % shards == g) else 0
+        bounds.append(nfull * PAGE + part)
+    return Problem(name=f"{p.name}_shard{g}of{shards}", q_bf16=p.q_bf16, w=p.w, k_e4m3=p.k_e4m3,
+                   k_scale=p.k_scale, page_table=np.ascontiguousarray(sub, dtype=np.int32),
+                   row_pt=p.row_pt, row_bound=np.array(bounds, dtype=np.int32), topk=p.topk,
+                   seed=p.seed)
+
+
 def device_arrays(p: Problem, device):
     """Torch tensors of a problem on ``device`` (plumbing for tests and bench)."""
     import torch
