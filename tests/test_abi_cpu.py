@@ -29,7 +29,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("indexer_score", "indexer_topk", "indexer_launch", "fp8idx_workspace_size",
-              "fp8idx_workspace_init", "fp8idx_abi_version", "fp8idx_strerror"):
+              "fp8idx_workspace_init", "fp8idx_abi_version", "fp8idx_strerror",
+              "indexer_shard_candidates", "indexer_merge_topk"):
         assert n in names
 
 
@@ -93,3 +94,34 @@ def test_host_side_argument_errors(lib):
     assert rc == -1   # out_idx missing
     assert lib.fp8idx_workspace_init(None, 256, None) == -1
     assert lib.fp8idx_workspace_init(0x100001, 256, None) == -1
+
+
+def test_sharded_selection_argument_errors(lib):
+    """Host-side checks of the key-sharded calls (nothing is launched: every
+    case fails before the device check)."""
+    import fp8_key_scoring_amd as fk
+    P = [0x1000, 0x2000, 0x3000, 0x4000]   # never dereferenced
+    ok = fk.make_problem(rows=4, num_pages=1, pt_rows=1, pt_stride=2048, max_bound=131072, topk=2048,
+                         score_stride=131072)
+    sc = lambda p, g, G, ptrs: lib.indexer_shard_candidates(ctypes.byref(p), g, G, *ptrs, None)
+    mg = lambda p, G, ptrs: lib.indexer_merge_topk(ctypes.byref(p), G, *ptrs, None)
+    for g, G in ((-1, 8), (8, 8), (0, 0), (0, 9)):        # shard outside [0, G); G * topk > 16384
+        assert sc(ok, g, G, P) == -1, (g, G)
+    for i in range(4):
+        ptrs = list(P)
+        ptrs[i] = None
+        assert sc(ok, 0, 8, ptrs) == -1
+    big = fk.make_problem(rows=4, num_pages=1, pt_rows=1, pt_stride=1 << 24, max_bound=(1 << 28),
+                          topk=2048, score_stride=1 << 28)
+    assert sc(big, 0, 8, P) == -1                          # global indices past int32
+    short = fk.make_problem(rows=4, num_pages=1, pt_rows=1, pt_stride=2048, max_bound=131072, topk=2048,
+                            score_stride=1000)
+    assert sc(short, 0, 8, P) == -1                        # score_stride < max_bound
+    assert mg(ok, 0, P[:3]) == -1 and mg(ok, 9, P[:3]) == -1
+    assert mg(ok, 8, [0x1004, 0x2000, 0x3000]) == -1       # candidates must be 16-byte aligned
+    odd = fk.make_problem(rows=4, num_pages=1, pt_rows=1, pt_stride=1, max_bound=0, topk=5)
+    assert mg(odd, 3, P[:3]) == -1                         # shards * topk not a multiple of 16
+    for i in range(3):
+        ptrs = list(P[:3])
+        ptrs[i] = None
+        assert mg(ok, 8, ptrs) == -1
