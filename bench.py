@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--shards", type=int, default=0,
                     help="time the key-sharded selection instead: one shard's launch, its "
                          "candidates and the merge of G shards (G GPUs emulated on one)")
+    ap.add_argument("--new-keys", action="store_true",
+                    help="time the launch with the new-key write instead: the write alone, the "
+                         "launch without and with it")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -243,6 +246,60 @@ def sharded_report(args):
                       "steps": args.steps}))
 
 
+def new_keys_report(args):
+    """The new-key write: each row's own key quantized and written at its last
+    position ahead of scoring.  Times, over back-to-back calls between events
+    on the launch stream (key pools rotated): the write alone, the ordinary
+    launch, and the combined call (write + launch)."""
+    import torch
+    import fp8_key_scoring_amd as fk
+    import synthetic as syn
+    fk.load_library()
+    dev = "cuda:0"
+    p = syn.make_config(args.config)
+    d = syn.device_arrays(p, dev)
+    pools = [d] + [{**d, "k_e4m3": d["k_e4m3"].clone(), "k_scale": d["k_scale"].clone(),
+                    "page_table": d["page_table"].clone()} for _ in range(1, args.pools)]
+    kn = torch.from_numpy(syn.new_keys(p, 0, special=False).view(np.int16)).to(dev).view(torch.bfloat16)
+    mb, k = p.max_bound, p.topk
+    prob = fk._problem_from(d["q"], d["k_e4m3"], d["page_table"], mb, k, 0)
+    ws = fk.new_workspace(prob, True, dev)
+    outs = torch.empty((p.rows, k), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n):
+        for i in range(min(args.warmup, n)):
+            fn(i)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    P = lambda i: pools[i % len(pools)]
+    # (the write alone is a four-wave kernel: back-to-back calls of it are
+    # bound by the host's call rate, so its figure is the call interval)
+    res = {"write_call_interval_us": [], "launch_us": [], "launch_new_keys_us": []}
+    for trial in range(5):
+        res["write_call_interval_us"].append(timed(lambda i: fk.indexer_write_keys(
+            kn, P(i)["k_e4m3"], P(i)["k_scale"], P(i)["page_table"], P(i)["row_pt"], P(i)["row_bound"],
+            max_bound=mb), args.steps))
+        res["launch_us"].append(timed(lambda i: fk.indexer_launch(**P(i), max_bound=mb, topk=k, out_idx=outs,
+                                                                  workspace=ws), args.steps))
+        res["launch_new_keys_us"].append(timed(lambda i: fk.indexer_launch_new_keys(
+            P(i)["q"], P(i)["w"], kn, P(i)["k_e4m3"], P(i)["k_scale"], P(i)["page_table"], P(i)["row_pt"],
+            P(i)["row_bound"], max_bound=mb, topk=k, out_idx=outs, workspace=ws), args.steps))
+    med = {key: round(float(np.median(v)), 2) for key, v in res.items()}
+    print(json.dumps({"metric": "launch with the new-key write: write, launch and combined µs",
+                      "config": {"workload": p.name, "rows": p.rows, "new_keys": p.rows, "topk": k},
+                      **med, "added_us": round(med["launch_new_keys_us"] - med["launch_us"], 2),
+                      "trials": 5, "steps": args.steps}))
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -254,6 +311,9 @@ def main():
         return
     if args.shards > 0:
         sharded_report(args)
+        return
+    if args.new_keys:
+        new_keys_report(args)
         return
     import torch
     import fp8_key_scoring_amd as fk

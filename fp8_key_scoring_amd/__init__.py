@@ -22,7 +22,8 @@ MAX_TOPK = 2048
 
 EXPORTED = ("fp8idx_abi_version", "fp8idx_strerror", "fp8idx_workspace_size",
             "fp8idx_workspace_init", "indexer_score", "indexer_topk", "indexer_launch",
-            "indexer_shard_candidates", "indexer_merge_topk")
+            "indexer_shard_candidates", "indexer_merge_topk", "indexer_write_keys",
+            "indexer_launch_new_keys")
 
 
 class Problem(ctypes.Structure):
@@ -71,6 +72,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.indexer_launch.restype = ctypes.c_int
     lib.indexer_launch.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, P, P,
                                    ctypes.c_size_t, P]
+    lib.indexer_write_keys.restype = ctypes.c_int
+    lib.indexer_write_keys.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P]
+    lib.indexer_launch_new_keys.restype = ctypes.c_int
+    lib.indexer_launch_new_keys.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, P, P,
+                                            P, ctypes.c_size_t, P]
     lib.indexer_shard_candidates.restype = ctypes.c_int
     lib.indexer_shard_candidates.argtypes = [ctypes.POINTER(Problem), ctypes.c_int, ctypes.c_int,
                                              P, P, P, P, P]
@@ -190,6 +196,53 @@ def indexer_launch(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound, *, max_
                                          _ptr(k_scale), _ptr(page_table), _ptr(row_pt),
                                          _ptr(row_bound), _ptr(scores), _ptr(out_idx),
                                          _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return out_idx
+
+
+def _check_new_keys(k_new, rows):
+    import torch
+    assert k_new.dtype == torch.bfloat16 and tuple(k_new.shape) == (rows, HEAD_DIM) and k_new.is_contiguous()
+
+
+def indexer_write_keys(k_new, k_e4m3, k_scale, page_table, row_pt, row_bound, *, max_bound: int):
+    """Quantizes each row's new key k_new [rows, 128] bf16 to E4M3 codes and a
+    scale and writes them in place into k_e4m3 / k_scale at the row's last
+    position (bound - 1).  Returns nothing."""
+    import torch
+    R = k_new.shape[0]
+    _check_new_keys(k_new, R)
+    assert k_e4m3.dtype == torch.uint8 and tuple(k_e4m3.shape[1:]) == (PAGE, HEAD_DIM) and k_e4m3.is_contiguous()
+    assert k_scale.dtype == torch.float32 and tuple(k_scale.shape) == (k_e4m3.shape[0], PAGE) and k_scale.is_contiguous()
+    assert page_table.dtype == torch.int32 and page_table.dim() == 2 and page_table.is_contiguous()
+    assert row_pt.dtype == torch.int32 and tuple(row_pt.shape) == (R,) and row_pt.is_contiguous()
+    assert row_bound.dtype == torch.int32 and tuple(row_bound.shape) == (R,) and row_bound.is_contiguous()
+    prob = make_problem(rows=R, num_pages=k_e4m3.shape[0], pt_rows=page_table.shape[0],
+                        pt_stride=page_table.shape[1], max_bound=max_bound, topk=MAX_TOPK, score_stride=0)
+    _check(load_library().indexer_write_keys(ctypes.byref(prob), _ptr(k_new), _ptr(k_e4m3), _ptr(k_scale),
+                                             _ptr(page_table), _ptr(row_pt), _ptr(row_bound),
+                                             _stream(k_new.device)))
+
+
+def indexer_launch_new_keys(q, w, k_new, k_e4m3, k_scale, page_table, row_pt, row_bound, *,
+                            max_bound: int, topk: int = MAX_TOPK, scores=None, out_idx=None,
+                            workspace=None):
+    """The new-key write (k_e4m3 / k_scale updated in place) followed by the
+    fused scoring + exact top-k.  Returns out_idx [rows, topk] int32."""
+    import torch
+    _check_inputs(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound)
+    R = q.shape[0]
+    _check_new_keys(k_new, R)
+    sstride = scores.stride(0) if scores is not None else 0
+    prob = _problem_from(q, k_e4m3, page_table, max_bound, topk, sstride)
+    if out_idx is None:
+        out_idx = torch.empty((R, topk), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(prob, scores is None, q.device)
+    _check(load_library().indexer_launch_new_keys(ctypes.byref(prob), _ptr(q), _ptr(w), _ptr(k_new),
+                                                  _ptr(k_e4m3), _ptr(k_scale), _ptr(page_table),
+                                                  _ptr(row_pt), _ptr(row_bound), _ptr(scores),
+                                                  _ptr(out_idx), _ptr(workspace), workspace.numel(),
+                                                  _stream(q.device)))
     return out_idx
 
 

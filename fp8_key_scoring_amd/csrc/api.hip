@@ -195,6 +195,44 @@ int indexer_launch(const fp8idx_problem_t *p, const void *q_bf16, const float *w
     return run_select(p, sc, sstride, row_bound, out_idx, wsb, L, false, st);
 }
 
+int indexer_write_keys(const fp8idx_problem_t *p, const void *k_new_bf16, uint8_t *k_e4m3,
+                       float *k_scale, const int32_t *page_table, const int32_t *row_pt,
+                       const int32_t *row_bound, void *stream) {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if (p->num_pages < 1 || p->pt_rows < 1 || p->pt_stride < 1) return FP8IDX_EINVAL;
+    if ((int64_t)p->max_bound > (int64_t)p->pt_stride * FP8IDX_PAGE) return FP8IDX_EINVAL;
+    if (!k_new_bf16 || !k_e4m3 || !k_scale || !page_table || !row_pt || !row_bound) return FP8IDX_EINVAL;
+    if (!aligned(k_new_bf16, 4) || !aligned(k_e4m3, 16) || !aligned(k_scale, 4) || !aligned(page_table, 4) ||
+        !aligned(row_pt, 4) || !aligned(row_bound, 4))
+        return FP8IDX_EINVAL;
+    rc = check_device();
+    if (rc) return rc;
+    return to_code(launch_write_keys((const uint16_t *)k_new_bf16, k_e4m3, k_scale, page_table, row_pt,
+                                     row_bound, p->rows, p->num_pages, p->pt_rows, p->pt_stride,
+                                     p->max_bound, (hipStream_t)stream));
+}
+
+int indexer_launch_new_keys(const fp8idx_problem_t *p, const void *q_bf16, const float *w,
+                            const void *k_new_bf16, uint8_t *k_e4m3, float *k_scale,
+                            const int32_t *page_table, const int32_t *row_pt, const int32_t *row_bound,
+                            float *scores, int32_t *out_idx, void *ws, size_t ws_bytes, void *stream) {
+    // every check of both steps before anything is enqueued
+    int rc = check_problem(p);
+    if (rc) return rc;
+    rc = check_score_inputs(p, q_bf16, w, k_e4m3, k_scale, page_table, row_pt, row_bound);
+    if (rc) return rc;
+    if (!k_new_bf16 || !aligned(k_new_bf16, 4)) return FP8IDX_EINVAL;
+    if (!out_idx || !aligned(out_idx, 4)) return FP8IDX_EINVAL;
+    if (scores && (!aligned(scores, 4) || p->score_stride < p->max_bound)) return FP8IDX_EINVAL;
+    const WsLayout L = ws_layout(p->rows, p->max_bound, scores == nullptr);
+    if (!ws || !aligned(ws, 256) || ws_bytes < L.total) return FP8IDX_EWORKSPACE;
+    rc = indexer_write_keys(p, k_new_bf16, k_e4m3, k_scale, page_table, row_pt, row_bound, stream);
+    if (rc) return rc;
+    return indexer_launch(p, q_bf16, w, k_e4m3, k_scale, page_table, row_pt, row_bound, scores, out_idx,
+                          ws, ws_bytes, stream);
+}
+
 static int check_shards(const fp8idx_problem_t *p, int shards) {
     if (shards < 1 || (int64_t)shards * p->topk > kMergeMaxCand) return FP8IDX_EINVAL;
     if ((int64_t)shards * ((int64_t)p->max_bound + FP8IDX_PAGE) >= ((int64_t)1 << 31)) return FP8IDX_EINVAL;

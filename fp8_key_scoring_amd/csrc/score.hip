@@ -60,11 +60,12 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
     return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// First-digit counters in LDS: [row slot][digit][64], one counter per lane
-// and digit, at position (lane + digit) % 64.  A wave's scores share only a
-// handful of first digits, so one counter per digit would make the lanes of
-// an atomic add collide; with the skew every lane of one add hits its own
-// bank, and the reduction (lane = digit, summing its 64 counters) does too.
+// First-digit counters in LDS: [row slot][digit][lane], one counter per lane
+// and digit.  A wave's scores share only a handful of first digits, so one
+// counter per digit would make the lanes of an atomic add collide; with a
+// counter per lane, lane l always adds into bank l whatever the digits.  The
+// reduction (lane = digit, summing its 64 counters) starts each lane at its
+// own counter and walks round, so its reads hit distinct banks as well.
 constexpr int kHistLds = kGroupRows * kBins1 * 64;   // u32 counters
 constexpr int kBlockPieces = kGroupRows * kHeads * kDim / 8 / kScoreThreads;   // q pieces per thread, 4 rows
 // Word 3 of a raw buffer resource for 32-bit accesses (32-bit data format).
@@ -342,8 +343,8 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
     // A block is one page of the wave: lane l holds the score of key
     // (first key of the page) + l, so each row's 64 scores go out as one
     // 256-byte store, masked at the row's bound, and (when counting) each
-    // lane adds its score's first radix digit to the row's LDS counters at
-    // position (lane + digit) % 64.
+    // lane adds its score's first radix digit to its own counter of that
+    // digit.
     auto flush = [&](int g) {   // g: the wave's index of the block's last group
         const int iq = g - 3 + lrow;
         const int s = j.group(iq) * kKeysPerMfma + kig;
@@ -362,7 +363,7 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), row, in_job ? (s - j.c0) * 4 : nrec, 0, 0);
             if (kHist) {   // every lane adds: 1 for a stored score, else 0 (no branch)
                 const uint32_t d = radix_key(out) >> kDigit1Shift;
-                atomicAdd(lds_cnt + (r * kBins1 + d) * 64 + ((lane + d) & 63),
+                atomicAdd(lds_cnt + (r * kBins1 + d) * 64 + lane,
                           (in_job && s < j.bnd[r]) ? 1u : 0u);
             }
         }

@@ -144,6 +144,39 @@ int indexer_launch(const fp8idx_problem_t *p,
                    float *scores, int32_t *out_idx,
                    void *ws, size_t ws_bytes, void *stream);
 
+/* ---- New keys (the same page, Modifications row 2 and the Reviewer notes
+ * on new keys: the launch writes keys into the cache and every row of the
+ * request scores them).  Row r's own key k_new[r] (128 bf16 elements) is
+ * quantized and written at logical position bound[r] - 1 of its page-table
+ * row: page page_table[row_pt[r]][(bound - 1) / 64], slot (bound - 1) % 64,
+ * 128 codes into k_e4m3 and one scale into k_scale.  Quantization (the pages
+ * give none; the plain per-key rule): scale = amax / 448 in fp32 with amax
+ * the key's largest magnitude (scale 1 and all codes 0 for an all-zero key),
+ * code = the OCP E4M3FN value nearest to the fp32 quotient k / scale, ties to
+ * the even code.  k_new elements must be finite.
+ *
+ * Layout: k_new [rows][128] bf16, 4-byte aligned.  A row with bound 0 (after
+ * clamping to [0, max_bound]), a page-table row outside [0, pt_rows) or a
+ * page id outside [0, num_pages) writes nothing.  When two rows name the same
+ * slot, which of their keys lands there is unspecified.  Errors: -1 for a
+ * null or misaligned pointer, or the problem checks of indexer_score. */
+int indexer_write_keys(const fp8idx_problem_t *p, const void *k_new_bf16,
+                       uint8_t *k_e4m3, float *k_scale,
+                       const int32_t *page_table, const int32_t *row_pt,
+                       const int32_t *row_bound, void *stream);
+
+/* indexer_write_keys followed by indexer_launch on the same stream: the rows
+ * score the cache with the launch's new keys in it (each row's own key and
+ * those of the rows before it in the request).  Arguments as for the two
+ * calls; every check of both happens before anything is enqueued. */
+int indexer_launch_new_keys(const fp8idx_problem_t *p,
+                            const void *q_bf16, const float *w, const void *k_new_bf16,
+                            uint8_t *k_e4m3, float *k_scale,
+                            const int32_t *page_table, const int32_t *row_pt,
+                            const int32_t *row_bound,
+                            float *scores, int32_t *out_idx,
+                            void *ws, size_t ws_bytes, void *stream);
+
 /* ---- Key-sharded selection (the context split over G shards by page).
  * Shard g of G (0 <= g < G) holds pages g, g+G, g+2G, ... of every request
  * in its own page table and runs indexer_launch (with `scores`) on them; its

@@ -50,6 +50,10 @@ def _load():
         lib.oracle_score_range.argtypes = [I, I64, I64, P, P, P, P, I, P, I, I, P, P, P, P]
         lib.oracle_score_samples.restype = I
         lib.oracle_score_samples.argtypes = [I64, P, P, P, P, P, P, I, P, I, I, P, P, P, P]
+        lib.oracle_quantize_key.restype = I
+        lib.oracle_quantize_key.argtypes = [P, P, P]
+        lib.oracle_e4m3_nearest.restype = ctypes.c_uint8
+        lib.oracle_e4m3_nearest.argtypes = [ctypes.c_float]
         lib.oracle_topk_f32.restype = I
         lib.oracle_topk_f32.argtypes = [P, I64, I, P]
         lib.oracle_topk_f64.restype = I
@@ -147,3 +151,51 @@ def merge_topk(cand_scores: np.ndarray, cand_idx: np.ndarray, k: int) -> np.ndar
     out = np.full(k, -1, dtype=np.int32)
     out[:sel.size] = sel
     return out
+
+
+def e4m3_nearest(x: float) -> int:
+    """The E4M3 code of one fp32 value: nearest finite code, ties to the even
+    mantissa, saturating at +-448 (oracle.c states the rule)."""
+    return int(_load().oracle_e4m3_nearest(ctypes.c_float(float(x))))
+
+
+def quantize_key(k_bf16: np.ndarray) -> Tuple[np.ndarray, np.float32]:
+    """One new key (128 raw bf16 patterns) -> its 128 E4M3 codes and fp32
+    scale (amax / 448; oracle.c states the rule)."""
+    k = np.ascontiguousarray(k_bf16, dtype=np.uint16).reshape(-1)
+    if k.size != 128:
+        raise ValueError("a key has 128 elements")
+    codes = np.empty(128, dtype=np.uint8)
+    sc = np.empty(1, dtype=np.float32)
+    rc = _load().oracle_quantize_key(_p(k), _p(codes), _p(sc))
+    if rc != 0:
+        raise RuntimeError(f"oracle_quantize_key failed: {rc}")
+    return codes, sc[0]
+
+
+def write_new_keys(p, k_new_bf16: np.ndarray):
+    """The launch's new-key write applied to host copies of the cache: row r
+    (in row order, so a later row wins a slot two rows name) writes its key
+    k_new[r] at logical position bound[r] - 1 of its page-table row, i.e.
+    page page_table[row_pt[r]][(bound - 1) // 64], slot (bound - 1) % 64.
+    A row with bound 0, a page-table row or page id out of range writes
+    nothing.  Returns (k_e4m3, k_scale) copies with the keys written; the
+    scores of the launch are then those of the written cache (the same page,
+    Reviewer notes "New keys": every row of the request that reaches the
+    position scores the new key)."""
+    k8 = np.array(p.k_e4m3, dtype=np.uint8, copy=True)
+    ks = np.array(p.k_scale, dtype=np.float32, copy=True)
+    kn = np.asarray(k_new_bf16, dtype=np.uint16).reshape(p.rows, 128)
+    pt = np.asarray(p.page_table)
+    for r in range(p.rows):
+        b = min(max(int(p.row_bound[r]), 0), int(p.max_bound))
+        pr = int(p.row_pt[r])
+        if b == 0 or pr < 0 or pr >= pt.shape[0]:
+            continue
+        page = int(pt[pr][(b - 1) // 64])
+        if page < 0 or page >= k8.shape[0]:
+            continue
+        codes, sc = quantize_key(kn[r])
+        k8[page, (b - 1) % 64, :] = codes
+        ks[page, (b - 1) % 64] = sc
+    return k8, ks

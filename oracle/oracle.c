@@ -254,3 +254,65 @@ int oracle_topk_f64(const double *scores, int64_t n, int k, int32_t *out)
     free(pr);
     return 0;
 }
+
+/* ---- New-key write (the same page, Modifications row 2 and the Reviewer
+ * notes "New keys": a key the launch itself writes is taken from its row's
+ * index_k8 pair, the key's E4M3 codes and scale, by every row of the request
+ * in the launch).  The pages give no quantization rule; the plain per-key one
+ * is taken: the scale is the key's largest magnitude over the largest finite
+ * E4M3 value, and each element divided by the scale goes to the nearest E4M3
+ * value.
+ *
+ *   amax  = max_i |k[i]|                 (the bf16 key decoded exactly)
+ *   scale = amax / 448                   (one fp32 division, round to nearest even)
+ *   x_i   = k[i] / scale                 (one fp32 division each)
+ *   code_i = the finite E4M3 code nearest to x_i; a tie goes to the code with
+ *            an even mantissa (its lowest bit clear); beyond 448 in magnitude
+ *            the code of +-448; the sign bit is x_i's sign bit (so -0 -> 0x80)
+ *   a key with amax == 0 gets scale 1 and all codes 0x00.
+ *
+ * The nearest code is found by looking at every non-negative finite code, as
+ * the definition reads (no bit manipulation).  Inputs are finite. */
+static uint8_t e4m3_nearest(float x)
+{
+    double a = fabs((double)x);
+    int best = 0, c;
+    double bestd = a;                 /* distance to code 0x00 (zero) */
+    for (c = 1; c <= 0x7E; ++c) {     /* every positive finite code */
+        double d = fabs(e4m3_value((uint8_t)c) - a);
+        if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) != 0)) {
+            best = c;
+            bestd = d;
+        }
+    }
+    if (a > 448.0)
+        best = 0x7E;
+    return (uint8_t)(best | (signbit(x) ? 0x80 : 0));
+}
+
+int oracle_quantize_key(const uint16_t *k_bf16, uint8_t *codes, float *scale_out)
+{
+    float kv[ORC_D], amax = 0.0f, scale;
+    int i;
+    if (!k_bf16 || !codes || !scale_out)
+        return -1;
+    for (i = 0; i < ORC_D; ++i) {
+        kv[i] = (float)bf16_value(k_bf16[i]);
+        if (fabsf(kv[i]) > amax)
+            amax = fabsf(kv[i]);
+    }
+    if (amax == 0.0f) {
+        memset(codes, 0, ORC_D);
+        *scale_out = 1.0f;
+        return 0;
+    }
+    scale = amax / 448.0f;
+    for (i = 0; i < ORC_D; ++i) {
+        volatile float x = kv[i] / scale;   /* an fp32 quotient, not a wider one */
+        codes[i] = e4m3_nearest(x);
+    }
+    *scale_out = scale;
+    return 0;
+}
+
+uint8_t oracle_e4m3_nearest(float x) { return e4m3_nearest(x); }

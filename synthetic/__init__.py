@@ -344,3 +344,26 @@ def device_arrays(p: Problem, device):
     return dict(q=t(p.q_bf16.view(np.int16)).view(torch.bfloat16), w=t(p.w),
                 k_e4m3=t(p.k_e4m3), k_scale=t(p.k_scale), page_table=t(p.page_table),
                 row_pt=t(p.row_pt), row_bound=t(p.row_bound))
+
+
+def new_keys(p: Problem, seed: int = 0, special: bool = True) -> np.ndarray:
+    """The launch's new keys, one per row: uint16 [rows, 128] raw bf16 of
+    fp32 N(0,1) draws (round to nearest even).  With `special`, the first rows
+    are edge keys: all zeros, one large element with tiny others (their
+    quotients fall into the E4M3 subnormals and below), exact E4M3 ties
+    after scaling (amax 448 makes the scale 1), and negative zeros."""
+    rng = np.random.default_rng(9000 + seed)
+    kf = rng.standard_normal((p.rows, 128)).astype(np.float32)
+    if special:
+        edge = []
+        edge.append(np.zeros(128, np.float32))                                  # amax 0
+        t = (rng.standard_normal(128) * 1e-3).astype(np.float32); t[5] = 300.0  # subnormal codes
+        edge.append(t)
+        t = np.full(128, 1.0625, np.float32); t[0] = 448.0                      # scale 1: ties
+        t[1:64:2] = 1.1875; t[2:64:4] = 3 * 2.0 ** -10; t[3:64:4] = -(2.0 ** -10)
+        edge.append(t)
+        t = rng.standard_normal(128).astype(np.float32); t[::3] = -0.0           # -0 elements
+        edge.append(t)
+        for i, e in enumerate(edge[:p.rows]):
+            kf[i] = e
+    return bf16_bits_rne(kf)

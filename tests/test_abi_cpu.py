@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("indexer_score", "indexer_topk", "indexer_launch", "fp8idx_workspace_size",
               "fp8idx_workspace_init", "fp8idx_abi_version", "fp8idx_strerror",
-              "indexer_shard_candidates", "indexer_merge_topk"):
+              "indexer_shard_candidates", "indexer_merge_topk", "indexer_write_keys",
+              "indexer_launch_new_keys"):
         assert n in names
 
 
@@ -125,3 +126,32 @@ def test_sharded_selection_argument_errors(lib):
         ptrs = list(P[:3])
         ptrs[i] = None
         assert mg(ok, 8, ptrs) == -1
+
+
+def test_new_key_argument_errors(lib):
+    """Host-side checks of the new-key calls (every case fails before the
+    device check, so nothing is launched)."""
+    import fp8_key_scoring_amd as fk
+    P = [0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000]   # k_new, k8, scale, pt, row_pt, bound
+    ok = fk.make_problem(rows=4, num_pages=16, pt_rows=1, pt_stride=16, max_bound=1024, topk=2048,
+                         score_stride=1024)
+    wk = lambda p, ptrs: lib.indexer_write_keys(ctypes.byref(p), *ptrs, None)
+    for i in range(6):
+        ptrs = list(P)
+        ptrs[i] = None
+        assert wk(ok, ptrs) == -1, i
+    for i, a in ((0, 0x1002), (1, 0x2008), (2, 0x3002)):    # k_new 4-, k_e4m3 16-, k_scale 4-byte aligned
+        ptrs = list(P)
+        ptrs[i] = a
+        assert wk(ok, ptrs) == -1, i
+    for b in (dict(rows=0), dict(num_pages=0), dict(pt_stride=0), dict(max_bound=16 * 64 + 1)):
+        assert wk(fk.make_problem(**{**dict(rows=4, num_pages=16, pt_rows=1, pt_stride=16, max_bound=1024,
+                                            topk=2048, score_stride=1024), **b}), P) == -1, b
+    # the combined call checks everything of both steps first
+    q, w = 0x7000, 0x8000
+    L = lambda p, kn, out, ws, wsb: lib.indexer_launch_new_keys(ctypes.byref(p), q, w, kn, *P[1:], None, out,
+                                                               ws, wsb, None)
+    assert L(ok, None, 0x9000, 0x100000, 1 << 30) == -1      # k_new missing
+    assert L(ok, 0x1002, 0x9000, 0x100000, 1 << 30) == -1    # k_new misaligned
+    assert L(ok, 0x1000, None, 0x100000, 1 << 30) == -1      # out_idx missing
+    assert L(ok, 0x1000, 0x9000, 0x100000, 16) == -2         # workspace too small
