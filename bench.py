@@ -113,9 +113,25 @@ def cpu_baseline(p, seconds):
         oracle.topk(np.concatenate(rows[r]), p.topk)
     wall = time.perf_counter() - t0
     n = keys_per_row * p.rows
+    # the same oracle on one core: row 0 alone, about a quarter of the CPU work
+    one_keys = int(min(p.row_bound[0], max(4096, seconds / 4 / per_key)))
+    one_keys -= one_keys % 1024
+    t0 = time.perf_counter()
+    sc1 = oracle.score_range(p, 0, 0, one_keys)[0]
+    oracle.topk(sc1, p.topk)
+    wall1 = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": n / wall, "unit": "keys/s", "cores": threads, "kind": "oracle",
             "sample": f"{p.rows} rows x first {keys_per_row} keys of the same workload: fp64 scores "
-                      f"+ exact top-{p.topk} of the sample, {threads} host threads, {wall:.2f} s"}
+                      f"+ exact top-{p.topk} of the sample, {threads} host threads, {wall:.2f} s",
+            "one_core": {"value": one_keys / wall1, "unit": "keys/s",
+                         "sample": f"row 0, first {one_keys} keys, one thread, {wall1:.2f} s"},
+            "cpu_model": model}
 
 
 def copy_calib():
