@@ -60,13 +60,15 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
     return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// First-digit counters in LDS: [row slot][digit][lane], one counter per lane
-// and digit.  A wave's scores share only a handful of first digits, so one
-// counter per digit would make the lanes of an atomic add collide; with a
-// counter per lane, lane l always adds into bank l whatever the digits.  The
-// reduction (lane = digit, summing its 64 counters) starts each lane at its
-// own counter and walks round, so its reads hit distinct banks as well.
-constexpr int kHistLds = kGroupRows * kBins1 * 64;   // u32 counters
+// First-digit counters in LDS: [wave][row slot][digit][4], each wave with its
+// own, lane l adding into copy l % 4 of its digit.  A wave's scores share only
+// a handful of first digits, so its lanes' adds collide on a few words; the
+// adds need no result, so the collisions cost LDS cycles the wave does not
+// wait for.  What the wave does wait for is the sum at the end of a row group
+// (lane = digit: four 16-byte reads, one per wave); with one counter per lane
+// and digit that sum read 64 words per lane and cost about 1.2 us more.
+constexpr int kCntCopies = 4;
+constexpr int kHistLds = (kScoreThreads / 64) * kGroupRows * kBins1 * kCntCopies;   // u32 counters
 constexpr int kBlockPieces = kGroupRows * kHeads * kDim / 8 / kScoreThreads;   // q pieces per thread, 4 rows
 // Word 3 of a raw buffer resource for 32-bit accesses (32-bit data format).
 constexpr int kBufferFlags = 0x00020000;
@@ -78,7 +80,7 @@ constexpr int kBufferFlags = 0x00020000;
 // workgroups return at once.)
 constexpr int kLdsQ = kGroupRows * kHeads * kDim * 2;     // 64 KB
 constexpr int kLdsT1 = 4 * 64 * 8 * 2;                   // [ks][lane][8] bf16, 4 KB
-static_assert(kHistLds * 4 == kLdsQ, "the counters reuse the q region");
+static_assert(kHistLds * 4 <= kLdsQ, "the counters reuse the q region");
 
 // The same pointer, held in scalar registers and opaque to the optimiser:
 // a load from it plus a 32-bit lane offset then uses the scalar-base
@@ -343,8 +345,7 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
     // A block is one page of the wave: lane l holds the score of key
     // (first key of the page) + l, so each row's 64 scores go out as one
     // 256-byte store, masked at the row's bound, and (when counting) each
-    // lane adds its score's first radix digit to its own counter of that
-    // digit.
+    // lane adds its score's first radix digit to its wave's counters.
     auto flush = [&](int g) {   // g: the wave's index of the block's last group
         const int iq = g - 3 + lrow;
         const int s = j.group(iq) * kKeysPerMfma + kig;
@@ -363,7 +364,7 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), row, in_job ? (s - j.c0) * 4 : nrec, 0, 0);
             if (kHist) {   // every lane adds: 1 for a stored score, else 0 (no branch)
                 const uint32_t d = radix_key(out) >> kDigit1Shift;
-                atomicAdd(lds_cnt + (r * kBins1 + d) * 64 + lane,
+                atomicAdd(lds_cnt + (((j.tid >> 6) * kGroupRows + r) * kBins1 + d) * kCntCopies + lane % kCntCopies,
                           (in_job && s < j.bnd[r]) ? 1u : 0u);
             }
         }
@@ -580,10 +581,12 @@ void score_kernel(ScoreArgs a) {
             __syncthreads();
             const int hr = tid >> 6;   // row slot; lane = digit
             if (hr < rg) {
-                const uint32_t *cnt = lds_cnt + (hr * kBins1 + job.lane) * 64;
                 uint32_t c = 0;
-#pragma unroll 16
-                for (int i = 0; i < 64; ++i) c += cnt[(i + job.lane) & 63];
+#pragma unroll
+                for (int w = 0; w < kScoreThreads / 64; ++w) {
+                    const u32x4_t v = *(const u32x4_t *)(lds_cnt + ((w * kGroupRows + hr) * kBins1 + job.lane) * kCntCopies);
+                    c += v[0] + v[1] + v[2] + v[3];
+                }
                 if (c) atomicAdd(a.hist1 + ((int64_t)(r0 + hr) * kHist1Slots + blockIdx.x % kHist1Slots) * kBins1 + job.lane, c);
             }
         }
