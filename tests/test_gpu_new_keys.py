@@ -127,3 +127,18 @@ def test_launch_new_keys_eight_row_request_and_a_second():
     p = syn.build_problem("newkeys_launch8", 34, [n, m], syn.verify_rows(0, n, 8) + syn.verify_rows(1, m, 3))
     kn = syn.new_keys(p, 6)
     _launch_case(p, kn)
+
+
+def test_launch_new_keys_many_requests():
+    # a batch of 24 requests of 4 verify rows each, lengths from 300 to
+    # 12,000 keys, one pool: every request's rows write and score their own
+    # new keys only
+    rng = np.random.default_rng(35)
+    lens = [int(x) for x in rng.integers(300, 12000, size=24)]
+    rows = []
+    for i, n in enumerate(lens):
+        rows += syn.verify_rows(i, n)
+    p = syn.build_problem("newkeys_batch", 35, lens, rows)
+    kn = syn.new_keys(p, 7)
+    say(f"[gpu] new keys, batch: rows={p.rows} requests={len(lens)}")
+    _launch_case(p, kn)
