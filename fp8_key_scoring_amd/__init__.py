@@ -23,7 +23,7 @@ MAX_TOPK = 2048
 EXPORTED = ("fp8idx_abi_version", "fp8idx_strerror", "fp8idx_workspace_size",
             "fp8idx_workspace_init", "indexer_score", "indexer_topk", "indexer_launch",
             "indexer_shard_candidates", "indexer_merge_topk", "indexer_write_keys",
-            "indexer_launch_new_keys")
+            "indexer_launch_new_keys", "indexer_validate")
 
 
 class Problem(ctypes.Structure):
@@ -72,6 +72,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.indexer_launch.restype = ctypes.c_int
     lib.indexer_launch.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, P, P,
                                    ctypes.c_size_t, P]
+    lib.indexer_validate.restype = ctypes.c_int
+    lib.indexer_validate.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P]
     lib.indexer_write_keys.restype = ctypes.c_int
     lib.indexer_write_keys.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P]
     lib.indexer_launch_new_keys.restype = ctypes.c_int
@@ -197,6 +199,28 @@ def indexer_launch(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound, *, max_
                                          _ptr(row_bound), _ptr(scores), _ptr(out_idx),
                                          _ptr(workspace), workspace.numel(), _stream(q.device)))
     return out_idx
+
+
+VALID_BOUND, VALID_ROW_PT, VALID_PAGE = 1, 2, 4
+
+
+def indexer_validate(page_table, row_pt, row_bound, *, max_bound: int, num_pages: int, status=None):
+    """Checks row_bound, row_pt and the page ids the rows would read; returns
+    the status tensor (one int32 on the device; bits VALID_BOUND,
+    VALID_ROW_PT, VALID_PAGE, 0 when every array is within range).  Nothing
+    synchronises: read it with ``.item()`` when needed."""
+    import torch
+    R = row_pt.shape[0]
+    assert page_table.dtype == torch.int32 and page_table.dim() == 2 and page_table.is_contiguous()
+    assert row_pt.dtype == torch.int32 and row_pt.is_contiguous()
+    assert row_bound.dtype == torch.int32 and tuple(row_bound.shape) == (R,) and row_bound.is_contiguous()
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=row_pt.device)
+    prob = make_problem(rows=R, num_pages=num_pages, pt_rows=page_table.shape[0], pt_stride=page_table.shape[1],
+                        max_bound=max_bound, topk=MAX_TOPK, score_stride=0)
+    _check(load_library().indexer_validate(ctypes.byref(prob), _ptr(page_table), _ptr(row_pt), _ptr(row_bound),
+                                           _ptr(status), _stream(row_pt.device)))
+    return status
 
 
 def _check_new_keys(k_new, rows):

@@ -195,6 +195,21 @@ int indexer_launch(const fp8idx_problem_t *p, const void *q_bf16, const float *w
     return run_select(p, sc, sstride, row_bound, out_idx, wsb, L, false, st);
 }
 
+int indexer_validate(const fp8idx_problem_t *p, const int32_t *page_table, const int32_t *row_pt,
+                     const int32_t *row_bound, uint32_t *status, void *stream) {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if (p->num_pages < 1 || p->pt_rows < 1 || p->pt_stride < 1) return FP8IDX_EINVAL;
+    if ((int64_t)p->max_bound > (int64_t)p->pt_stride * FP8IDX_PAGE) return FP8IDX_EINVAL;
+    if (!page_table || !row_pt || !row_bound || !status) return FP8IDX_EINVAL;
+    if (!aligned(page_table, 4) || !aligned(row_pt, 4) || !aligned(row_bound, 4) || !aligned(status, 4))
+        return FP8IDX_EINVAL;
+    rc = check_device();
+    if (rc) return rc;
+    return to_code(launch_validate(page_table, row_pt, row_bound, status, p->rows, p->num_pages, p->pt_rows,
+                                   p->pt_stride, p->max_bound, (hipStream_t)stream));
+}
+
 int indexer_write_keys(const fp8idx_problem_t *p, const void *k_new_bf16, uint8_t *k_e4m3,
                        float *k_scale, const int32_t *page_table, const int32_t *row_pt,
                        const int32_t *row_bound, void *stream) {

@@ -154,6 +154,9 @@ hipError_t launch_shard_cand(const float *scores, int64_t sstride, const int32_t
 hipError_t launch_merge(int rows, int n, int k, const float *cand_score, const int32_t *cand_idx,
                         int32_t *out_idx, hipStream_t st);
 constexpr int kMergeMaxCand = 16384;   // shards * topk the merge holds per row
+hipError_t launch_validate(const int32_t *page_table, const int32_t *row_pt, const int32_t *row_bound,
+                           uint32_t *status, int rows, int num_pages, int pt_rows, int pt_stride, int max_bound,
+                           hipStream_t st);
 hipError_t launch_write_keys(const uint16_t *k_new, uint8_t *k8, float *kscale, const int32_t *page_table,
                              const int32_t *row_pt, const int32_t *row_bound, int rows, int num_pages,
                              int pt_rows, int pt_stride, int max_bound, hipStream_t st);

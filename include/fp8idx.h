@@ -144,6 +144,20 @@ int indexer_launch(const fp8idx_problem_t *p,
                    float *scores, int32_t *out_idx,
                    void *ws, size_t ws_bytes, void *stream);
 
+/* Checks the device arrays the calls above trust and writes a status word to
+ * `status` (one device uint32, 4-byte aligned; zeroed by this call first, then
+ * OR-ed): bit 0 (1) some row_bound outside [0, max_bound]; bit 1 (2) some
+ * row_pt outside [0, pt_rows); bit 2 (4) some page id a row would read (its
+ * page-table entries below ceil(min(bound, max_bound) / 64)) outside
+ * [0, num_pages).  0 = every array is within range.  The launches stay safe
+ * on such values (bounds clamped, bad page-table rows or page ids score NaN);
+ * this call reports them, in place of a separate debug build.  Uses p->rows,
+ * num_pages, pt_rows, pt_stride, max_bound.  Errors: -1 for a null or
+ * misaligned pointer or the problem checks of indexer_score.  No workspace. */
+int indexer_validate(const fp8idx_problem_t *p, const int32_t *page_table,
+                     const int32_t *row_pt, const int32_t *row_bound,
+                     uint32_t *status, void *stream);
+
 /* ---- New keys (the same page, Modifications row 2 and the Reviewer notes
  * on new keys: the launch writes keys into the cache and every row of the
  * request scores them).  Row r's own key k_new[r] (128 bf16 elements) is

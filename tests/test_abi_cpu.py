@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     for n in ("indexer_score", "indexer_topk", "indexer_launch", "fp8idx_workspace_size",
               "fp8idx_workspace_init", "fp8idx_abi_version", "fp8idx_strerror",
               "indexer_shard_candidates", "indexer_merge_topk", "indexer_write_keys",
-              "indexer_launch_new_keys"):
+              "indexer_launch_new_keys", "indexer_validate"):
         assert n in names
 
 
@@ -155,3 +155,19 @@ def test_new_key_argument_errors(lib):
     assert L(ok, 0x1002, 0x9000, 0x100000, 1 << 30) == -1    # k_new misaligned
     assert L(ok, 0x1000, None, 0x100000, 1 << 30) == -1      # out_idx missing
     assert L(ok, 0x1000, 0x9000, 0x100000, 16) == -2         # workspace too small
+
+
+def test_validate_argument_errors(lib):
+    import fp8_key_scoring_amd as fk
+    P = [0x1000, 0x2000, 0x3000, 0x4000]   # page_table, row_pt, row_bound, status (never dereferenced)
+    ok = fk.make_problem(rows=4, num_pages=16, pt_rows=1, pt_stride=16, max_bound=1024, topk=2048)
+    v = lambda p, ptrs: lib.indexer_validate(ctypes.byref(p), *ptrs, None)
+    for i in range(4):
+        ptrs = list(P)
+        ptrs[i] = None
+        assert v(ok, ptrs) == -1, i
+    ptrs = list(P)
+    ptrs[3] = 0x4002                                      # status must be 4-byte aligned
+    assert v(ok, ptrs) == -1
+    bad = fk.make_problem(rows=4, num_pages=16, pt_rows=1, pt_stride=16, max_bound=16 * 64 + 1, topk=2048)
+    assert v(bad, P) == -1

@@ -105,3 +105,29 @@ def test_out_of_range_page_ids_score_nan():
         assert np.all(np.isfinite(scores[r, :b][~bad[:b]]))
     check_topk_exact(p, scores, out)
     assert not np.any(bad[out[out >= 0]])
+
+
+def test_validate_reports_each_kind_of_bad_array():
+    import torch
+    p = syn.build_problem("validate", 41, [3000, 700], [(0, 3000), (0, 2999), (1, 700), (1, 64)])
+    def status(pt, rp, rb, mb=None):
+        st = fk.indexer_validate(torch.from_numpy(pt).to("cuda:0"), torch.from_numpy(rp).to("cuda:0"),
+                                 torch.from_numpy(rb).to("cuda:0"), max_bound=p.max_bound if mb is None else mb,
+                                 num_pages=p.num_pages)
+        return int(st.item())
+    pt, rp, rb = p.page_table.copy(), p.row_pt.copy(), p.row_bound.copy()
+    assert status(pt, rp, rb) == 0
+    rb2 = rb.copy(); rb2[3] = -5
+    assert status(pt, rp, rb2) == fk.VALID_BOUND
+    rb3 = rb.copy(); rb3[0] = p.max_bound + 1                 # past max_bound
+    assert status(pt, rp, rb3) == fk.VALID_BOUND
+    rp2 = rp.copy(); rp2[2] = pt.shape[0]
+    assert status(pt, rp2, rb) == fk.VALID_ROW_PT
+    pt2 = pt.copy(); pt2[1, 5] = p.num_pages                  # row 2 reads page 5 of request 1
+    assert status(pt2, rp, rb) == fk.VALID_PAGE
+    pt3 = pt.copy(); pt3[1, 10] = -1                          # page 10 of request 1 (keys 640..699)
+    assert status(pt3, rp, rb) == fk.VALID_PAGE               # row 2 (bound 700) reads it
+    rb4 = rb.copy(); rb4[2] = 640
+    assert status(pt3, rp, rb4) == 0                          # with bound 640 no row reads it
+    both = rb.copy(); both[1] = -1
+    assert status(pt2, rp2, both) == fk.VALID_BOUND | fk.VALID_ROW_PT   # row 2's pages are not read: its pt row is bad
