@@ -131,3 +131,31 @@ def test_validate_reports_each_kind_of_bad_array():
     assert status(pt3, rp, rb4) == 0                          # with bound 640 no row reads it
     both = rb.copy(); both[1] = -1
     assert status(pt2, rp2, both) == fk.VALID_BOUND | fk.VALID_ROW_PT   # row 2's pages are not read: its pt row is bad
+
+
+def _zero_block_bytes(rows):
+    """Bytes of the workspace's zero block (the three digit histograms), the
+    part every launch must find zero and leaves zero; the rest is scratch a
+    launch writes before it reads (sizes as the library lays them out)."""
+    al = lambda x: (x + 255) // 256 * 256
+    rz = max(rows, 1024)
+    return al(rz * 16 * 64 * 4) + al(rz * 8 * 256 * 4) + al(rz * 256 * 4)
+
+
+def test_poisoned_scratch_gives_the_same_bytes():
+    # 0xFF in every scratch byte (NaN scores, huge counts, garbage lists):
+    # the launch must not read scratch it has not written
+    say("[gpu] poisoned scratch")
+    for p in (_prob(28, n=70000), syn.build_problem("poison_ties", 29, [9000], syn.verify_rows(0, 9000),
+                                                    dup_frac=0.3)):
+        ref_scores, ref = run_launch(p)
+        prob = fk.make_problem(rows=p.rows, num_pages=p.num_pages, pt_rows=p.page_table.shape[0],
+                               pt_stride=p.pt_stride, max_bound=p.max_bound, topk=p.topk)
+        ws = fk.new_workspace(prob, True, "cuda:0")
+        z = _zero_block_bytes(p.rows)
+        assert ws.numel() > z
+        for _ in range(2):
+            ws[z:].fill_(255)
+            _, o = run_launch(p, keep_scores=False, workspace=ws)
+            assert np.array_equal(o, ref)
+            assert not ws[:z].any()            # the zero block is left zero
