@@ -142,3 +142,25 @@ def test_launch_new_keys_many_requests():
     kn = syn.new_keys(p, 7)
     say(f"[gpu] new keys, batch: rows={p.rows} requests={len(lens)}")
     _launch_case(p, kn)
+
+
+def test_write_hand_worked_cases():
+    # the hand-worked quantizations of tests/golden/quant_hand_cases.json,
+    # written by the GPU and read back from the cache
+    import json, os
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "quant_hand_cases.json")))["cases"]
+    n = 64 * 4
+    p = syn.build_problem("newkeys_hand", 36, [n], [(0, 10 + 70 * i) for i in range(len(cases))])
+    kn = np.zeros((p.rows, 128), np.uint16)
+    for r, case in enumerate(cases):
+        for i, bits in case["k_bf16_bits"].items():
+            kn[r, int(i)] = int(bits, 16)
+    k8, ks = _write_on_gpu(p, kn)
+    for r, case in enumerate(cases):
+        pos = int(p.row_bound[r]) - 1
+        page = int(p.page_table[0][pos // 64])
+        want = np.zeros(128, np.uint8)
+        for i, c in case["codes"].items():
+            want[int(i)] = int(c, 16)
+        assert np.array_equal(k8[page, pos % 64], want), case["name"]
+        assert int(ks[page, pos % 64:pos % 64 + 1].view(np.uint32)[0]) == int(case["scale_bits"], 16), case["name"]

@@ -9,7 +9,9 @@ conversion (a library routine, round to nearest even) on many values, to
 hand-worked ties, and to the bounds the rule implies; the write step to hand
 positions, page crossings and the skip cases.
 """
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -114,3 +116,19 @@ def test_new_key_generator_edges():
     assert kn.shape == (6, 128) and kn.dtype == np.uint16
     assert not (kn[0] & 0x7FFF).any()                              # the all-zero key
     assert ((kn[3] == 0x8000).sum()) >= 40                          # negative zeros
+
+
+def test_hand_worked_quantizations(oracle_lib):
+    """tests/golden/quant_hand_cases.json: quantizations worked out by hand
+    from the rule (the arithmetic is in each case's 'why')."""
+    path = os.path.join(os.path.dirname(__file__), "golden", "quant_hand_cases.json")
+    for case in json.load(open(path))["cases"]:
+        k = np.zeros(128, np.uint16)
+        for i, bits in case["k_bf16_bits"].items():
+            k[int(i)] = int(bits, 16)
+        codes, sc = oracle_lib.quantize_key(k)
+        assert int(np.array([sc], np.float32).view(np.uint32)[0]) == int(case["scale_bits"], 16), case["name"]
+        want = np.zeros(128, np.uint8)
+        for i, c in case["codes"].items():
+            want[int(i)] = int(c, 16)
+        assert np.array_equal(codes, want), case["name"]
