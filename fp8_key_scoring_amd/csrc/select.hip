@@ -91,30 +91,24 @@ __device__ void wave_scan128(uint32_t *c, uint32_t *total, int lane) {
     if (lane == 63) *total = incl;
 }
 
-// Exclusive prefix sum of v over the workgroup in thread order (*total: the sum).
-__device__ uint32_t block_scan(uint32_t v, uint32_t *wsum, uint32_t *total) {
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    uint32_t incl = v;
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
+// Exclusive prefix over the workgroup, in thread order, of a v < 8 per
+// thread: within a wave three ballots (one per bit of v) and their lane
+// prefixes, across waves one barrier and the wave totals.  wsum must not be
+// written again by the workgroup after this call.
+__device__ uint32_t block_scan_small(uint32_t v, uint32_t *wsum) {
+    const int t = threadIdx.x, wave = t >> 6;
+    uint32_t pre = 0, tot = 0;
+#pragma unroll
+    for (int bit = 0; bit < 3; ++bit) {
+        const uint64_t m = __ballot((v >> bit) & 1u);
+        pre += lane_prefix(m) << bit;
+        tot += (uint32_t)__popcll(m) << bit;
     }
-    if (lane == 63) wsum[wave] = incl;
+    if ((t & 63) == 0) wsum[wave] = tot;
     __syncthreads();
-    if (t < 64) {
-        const uint32_t w = lane < kWaves ? wsum[lane] : 0u;
-        uint32_t wi = w;
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t y = __shfl_up(wi, off);
-            if (lane >= off) wi += y;
-        }
-        if (lane < kWaves) wsum[lane] = wi - w;
-        if (lane == kWaves - 1) *total = wi;
-    }
-    __syncthreads();
-    const uint32_t r = wsum[wave] + incl - v;
-    __syncthreads();
-    return r;
+    uint32_t off = 0;
+    for (int w = 0; w < wave; ++w) off += wsum[w];
+    return off + pre;
 }
 
 // Radix keys of keys base + j*kSelThreads + t (j < kSelUnroll) into
@@ -444,36 +438,40 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
     __shared__ uint32_t h3[kBins3];
     __shared__ uint32_t wsum[kWaves], wtie[kWaves];
     __shared__ int sB;
-    __shared__ uint32_t sAbove, ntie, ovf, total;
+    __shared__ uint32_t sAbove, ntie, ovf;
     constexpr int kPer = kEntCap / kSelThreads;   // entries per thread
     constexpr int kPre = 4;                       // entries per thread loaded ahead of the counts
+    static_assert(kPer < 8, "finalize: a thread's kept count fits the three-bit scan");
     static_assert(kEntCap % kSelThreads == 0, "finalize: whole entries per thread");
     static_assert(kSelMaxWgs * 16 == kSelThreads, "finalize: 16 threads per slice");
     const int r = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int b = clamp_bound(a.row_bound[r], a.max_bound);
     const int k = a.topk;
     const int S = a.L.sel_wgs;
     int32_t *out_row = a.out_idx + (int64_t)r * k;
     uint32_t *hist3 = (uint32_t *)(a.ws + a.L.hist3) + (int64_t)r * kBins3;
+    // Every load goes out before any is waited on, the row's bound included
+    // (one workgroup per row, so none of them is wasted but for rows whose
+    // keys are all selected, where the state and lists are stale and unused):
+    // the bound, the state, the third digits, the per-slice counts and,
+    // without waiting for those, the first 64 entries of every slice (16
+    // threads per slice), which is all of a slice in the usual case.
+    const int b_raw = a.row_bound[r];
+    const uint32_t *ecnt = (const uint32_t *)(a.ws + a.L.ent_cnt) + (int64_t)r * S;
+    const uint32_t *ccnt = (const uint32_t *)(a.ws + a.L.cand_cnt) + (int64_t)r * S;
+    const unsigned long long *sl = (const unsigned long long *)(a.ws + a.L.ent_list) + (int64_t)r * S * kSliceCap;
+    const int x = t >> 4, j0 = t & 15;
+    const int xs = x < S ? x : 0;
+    const RowState st = ((const RowState *)(a.ws + a.L.state))[r];
+    const uint32_t h3v = hist3[t & (kBins3 - 1)];
+    const uint32_t ne = ecnt[lane < S ? lane : 0], ncx = ccnt[lane < S ? lane : 0];
+    unsigned long long pre[kPre];
+#pragma unroll
+    for (int m = 0; m < kPre; ++m) pre[m] = sl[(int64_t)xs * kSliceCap + j0 + 16 * m];
+    __builtin_amdgcn_sched_barrier(0);
+    const int b = clamp_bound(b_raw, a.max_bound);
     if (b > k) {
-        const uint32_t *ecnt = (const uint32_t *)(a.ws + a.L.ent_cnt) + (int64_t)r * S;
-        const uint32_t *ccnt = (const uint32_t *)(a.ws + a.L.cand_cnt) + (int64_t)r * S;
-        const unsigned long long *sl = (const unsigned long long *)(a.ws + a.L.ent_list) + (int64_t)r * S * kSliceCap;
-        // Every load goes out before any is waited on: the state, the third
-        // digits, the per-slice counts and, without waiting for those, the
-        // first 64 entries of every slice (16 threads per slice), which is
-        // all of a slice in the usual case.
-        const int x = t >> 4, j0 = t & 15;
-        const int xs = x < S ? x : 0;
-        const RowState st = ((const RowState *)(a.ws + a.L.state))[r];
-        const uint32_t h3v = hist3[t & (kBins3 - 1)];
         // slices that start at or past the bound were not written: empty
         const bool live = lane < S && (int64_t)lane * a.L.sel_chunk < b;
-        const uint32_t ne = ecnt[lane < S ? lane : 0], ncx = ccnt[lane < S ? lane : 0];
-        unsigned long long pre[kPre];
-#pragma unroll
-        for (int m = 0; m < kPre; ++m) pre[m] = sl[(int64_t)xs * kSliceCap + j0 + 16 * m];
-        __builtin_amdgcn_sched_barrier(0);
         const int need = (int)(st.need < (uint32_t)kMaxTopk ? st.need : (uint32_t)kMaxTopk);
         const uint32_t T14 = (st.b1 << kDigit2Bits) | st.b2;
         // slice offsets (exclusive prefix of the entry counts); candidates
@@ -583,7 +581,7 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
                 }
                 cnt += kept[q];
             }
-            uint32_t pos = block_scan(cnt, wsum, &total);
+            uint32_t pos = block_scan_small(cnt, wsum);
 #pragma unroll
             for (int q = 0; q < kPer; ++q)
                 if (kept[q]) {
