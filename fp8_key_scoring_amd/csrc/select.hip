@@ -184,10 +184,12 @@ __global__ __launch_bounds__(kSelThreads) void hist1_kernel(SelectArgs a) {
 
 // ---------------------------------------------------------------- refine
 // Second-digit counts inside the first-digit bin of the k-th largest key.
-// One LDS copy per wave keeps the waves' atomics off each other's words.
+// Four LDS copies (wave % 4) keep the waves' atomics apart; with one copy per
+// wave the zeroing and the final sum over 16 copies cost more than the
+// collisions they avoid (C5's launch 3 us longer).
 __global__ __launch_bounds__(kSelThreads) void refine_kernel(SelectArgs a) {
     __shared__ uint32_t h1[kBins1];
-    __shared__ uint32_t h2[kWaves][kBins2];
+    __shared__ uint32_t h2[4][kBins2];
     __shared__ int sb1;
     __shared__ uint32_t sabove1;
     const int r = blockIdx.y, x = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(kSelThreads) void refine_kernel(SelectArgs a) {
     load_raw(row, s0, s1, v0);
     __builtin_amdgcn_sched_barrier(0);
     if (t < kBins1) h1[t] = hist1_sum(c1);
-    for (int i = t; i < kWaves * kBins2; i += kSelThreads) (&h2[0][0])[i] = 0;
+    for (int i = t; i < 4 * kBins2; i += kSelThreads) (&h2[0][0])[i] = 0;
     if (t == 0) { sb1 = 0; sabove1 = 0; }
     __syncthreads();
     if (t < 64) wave_find_bin(h1, 1, k, lane, &sb1, &sabove1);
@@ -226,12 +228,12 @@ __global__ __launch_bounds__(kSelThreads) void refine_kernel(SelectArgs a) {
 #pragma unroll
         for (int j = 0; j < kSelUnroll; ++j)
             if (base + j * kSelThreads + t < s1 && (u[j] >> kDigit1Shift) == b1)
-                atomicAdd(&h2[wave][(u[j] >> kDigit2Shift) & (kBins2 - 1)], 1u);
+                atomicAdd(&h2[wave & 3][(u[j] >> kDigit2Shift) & (kBins2 - 1)], 1u);
     }
     __syncthreads();
     if (t < kBins2) {
         uint32_t c = 0;
-        for (int w = 0; w < kWaves; ++w) c += h2[w][t];
+        for (int w = 0; w < 4; ++w) c += h2[w][t];
         if (c) atomicAdd((uint32_t *)(a.ws + a.L.hist2) + ((int64_t)r * kHist2Slots + x % kHist2Slots) * kBins2 + t, c);
     }
 }
