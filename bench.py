@@ -319,7 +319,7 @@ def new_keys_report(args):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build times the single-GPU indexer launch "
+        print("bench.py runs on one GPU only: it times the indexer launch on a single GPU "
               "(use --gpus 1)", file=sys.stderr)
         sys.exit(2)
     if args.copy_calib:
