@@ -156,3 +156,24 @@ def test_c6_one_row_512k():
 def test_c7_two_rows_512k():
     # a two-row group over a long context
     _big(7)
+
+
+def test_one_row_1200k_multi_step_slices():
+    # a row longer than 64 x 8,192 keys: each selection workgroup scans
+    # several 8K-key steps of its slice (refine's and gather's step loop
+    # past the first step), and the scoring grid has 293 chunks of 4,096
+    n = 1_200_000
+    p = syn.build_problem("row_1200k", 37, [n], [(0, n)], dup_frac=0.01)
+    full_check(p, "row_1200k")
+
+
+def test_1100_rows_more_than_the_zero_block_layout():
+    # more rows than the 1,024 the workspace's zero block is laid out for by
+    # default: the block is then sized by the row count
+    lens = [300 + (i * 37) % 2900 for i in range(275)]
+    rows = []
+    for i, n in enumerate(lens):
+        rows += syn.verify_rows(i, n)
+    p = syn.build_problem("rows_1100", 38, lens, rows)
+    assert p.rows == 1100
+    full_check(p, "rows_1100")
