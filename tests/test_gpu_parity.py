@@ -164,7 +164,16 @@ def test_one_row_1200k_multi_step_slices():
     # past the first step), and the scoring grid has 293 chunks of 4,096
     n = 1_200_000
     p = syn.build_problem("row_1200k", 37, [n], [(0, n)], dup_frac=0.01)
-    full_check(p, "row_1200k")
+    scores, out = full_check(p, "row_1200k")
+    # the selection alone (its own first-digit pass over several steps per
+    # workgroup) on the same scores gives the same bytes
+    import torch
+    import fp8_key_scoring_amd as fk
+    sc = torch.from_numpy(np.ascontiguousarray(scores)).to("cuda:0")
+    rb = torch.from_numpy(p.row_bound.copy()).to("cuda:0")
+    o2 = fk.indexer_topk(sc, rb, max_bound=p.max_bound, topk=p.topk)
+    torch.cuda.synchronize()
+    assert np.array_equal(o2.cpu().numpy(), out)
 
 
 def test_1100_rows_more_than_the_zero_block_layout():
