@@ -171,3 +171,27 @@ def test_validate_argument_errors(lib):
     assert v(ok, ptrs) == -1
     bad = fk.make_problem(rows=4, num_pages=16, pt_rows=1, pt_stride=16, max_bound=16 * 64 + 1, topk=2048)
     assert v(bad, P) == -1
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/fp8idx.h compiles as C99 with gcc (no HIP or C++ types in the
+    boundary), and a C program taking the address of every entry point links
+    against the built library."""
+    import shutil
+    import subprocess
+    import fp8_key_scoring_amd as fk
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not installed")
+    src = tmp_path / "use_abi.c"
+    names = declared_functions()
+    body = "\n".join(f"    p[{i}] = (void (*)(void))&{n};" for i, n in enumerate(names))
+    src.write_text('#include "fp8idx.h"\n#include <stdio.h>\n'
+                   f"int main(void) {{\n    void (*p[{len(names)}])(void);\n{body}\n"
+                   "    fp8idx_problem_t prob = {0};\n    (void)prob;\n"
+                   '    printf("%d\\n", fp8idx_abi_version());\n    return p[0] == 0;\n}\n')
+    exe = tmp_path / "use_abi"
+    lib = fk.LIB_PATH
+    cmd = ["gcc", "-std=c99", "-Wall", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"), str(src),
+           "-o", str(exe), lib, "-Wl,-rpath," + os.path.dirname(lib)]
+    out = subprocess.run(cmd, capture_output=True, text=True)
+    assert out.returncode == 0, out.stderr[-2000:]
