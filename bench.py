@@ -388,6 +388,36 @@ def main():
     torch.cuda.synchronize()
     ms_step_hot = e0.elapsed_time(e1) / args.steps
 
+    # the same launches replayed from a HIP graph: one graph holds a launch on
+    # each key pool; replaying it back to back removes the host's per-call
+    # work (the launch enqueues kernels only, so it can be captured)
+    us_graph = None
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for i in range(len(pools)):
+                step(i)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(len(pools)):
+                step(i)
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // len(pools))
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us_graph = e0.elapsed_time(e1) * 1e3 / (reps * len(pools))
+    except RuntimeError as exc:   # a runtime without stream capture: report none
+        print(f"graph replay not measured: {exc}", file=sys.stderr)
+
     # scoring kernel alone: n_k back-to-back launches (rotating key pools)
     # between two events on the launch stream; the mean is the kernel's
     # average duration (the launches add no gaps of their own)
@@ -435,6 +465,7 @@ def main():
         "ms_per_step": ms_step,
         "us_per_launch": ms_step * 1e3,
         "us_per_launch_hot": ms_step_hot * 1e3,
+        "us_per_launch_graph": None if us_graph is None else round(us_graph, 2),
         "us_per_launch_trials": {"n": n_trials, "median": round(trial_us[n_trials // 2], 2),
                                  "min": round(trial_us[0], 2), "max": round(trial_us[-1], 2)},
         "launch_roofline_frac": round(step_roof_s / (ms_step * 1e-3), 4),
