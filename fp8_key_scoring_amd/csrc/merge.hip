@@ -46,39 +46,40 @@ __global__ __launch_bounds__(256) void shard_cand_kernel(const float *scores, in
     }
 }
 
-// Exclusive prefix over the workgroup of one value per thread (thread
-// order); *total receives the sum.
-__device__ uint32_t merge_scan(uint32_t v, uint32_t *wsum, uint32_t *total) {
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    uint32_t incl = v;
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
+// Exclusive prefix over the workgroup, in thread order, of a v <= 16 per
+// thread: within a wave five ballots (one per bit of v) and their lane
+// prefixes, across waves one barrier and the wave totals; `total` receives
+// the sum in every thread.  wsum (one word per wave) must not be written
+// again until every thread has returned.
+__device__ uint32_t merge_scan(uint32_t v, uint32_t *wsum, uint32_t &total) {
+    const int t = threadIdx.x, wave = t >> 6;
+    uint32_t pre = 0, tot = 0;
+#pragma unroll
+    for (int bit = 0; bit < 5; ++bit) {
+        const uint64_t m = __ballot((v >> bit) & 1u);
+        pre += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << bit;
+        tot += (uint32_t)__popcll(m) << bit;
     }
-    if (lane == 63) wsum[wave] = incl;
+    if ((t & 63) == 0) wsum[wave] = tot;
     __syncthreads();
-    if (t < 64) {
-        const uint32_t w = lane < kMergeThreads / 64 ? wsum[lane] : 0u;
-        uint32_t wi = w;
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t y = __shfl_up(wi, off);
-            if (lane >= off) wi += y;
-        }
-        if (lane < kMergeThreads / 64) wsum[lane] = wi - w;
-        if (lane == kMergeThreads / 64 - 1) *total = wi;
+    uint32_t off = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kMergeThreads / 64; ++w) {
+        const uint32_t x = wsum[w];
+        off += w < wave ? x : 0u;
+        all += x;
     }
-    __syncthreads();
-    const uint32_t r = wsum[wave] + incl - v;
-    __syncthreads();
-    return r;
+    total = all;
+    return off + pre;
 }
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(int n, int k, const float *cand_score,
                                                               const int32_t *cand_idx, int32_t *out_idx) {
     __shared__ uint32_t hist[kMergeBins];
-    __shared__ uint32_t wsum[kMergeThreads / 64];
+    __shared__ uint32_t wsum[kMergeThreads / 64], wsum2[kMergeThreads / 64];   // one per scan
     __shared__ uint64_t wmin[kMergeThreads / 64], wmax[kMergeThreads / 64];
-    __shared__ uint32_t s_total, s_bin, s_above, s_cnt;
+    __shared__ uint32_t s_bin, s_above, s_cnt;
+    static_assert(kMergePer <= 16, "merge: a thread's counts fit the five-bit scan");
     const int r = blockIdx.x, t = threadIdx.x, lane = t & 63;
     const float *sc = cand_score + (int64_t)r * n;
     const int32_t *ix = cand_idx + (int64_t)r * n;
@@ -107,8 +108,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(int n, int k, cons
             valid += id >= 0;
         }
     }
-    (void)merge_scan(valid, wsum, &s_total);   // the row's valid candidates
-    const uint32_t total_valid = s_total;
+    uint32_t total_valid;   // the row's valid candidates
+    (void)merge_scan(valid, wsum, total_valid);
     const uint32_t want = total_valid < (uint32_t)k ? total_valid : (uint32_t)k;
 
     // The candidates are the shards' top-k: their scores crowd into a narrow
@@ -203,7 +204,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(int n, int k, cons
 #pragma unroll
     for (int m = 0; m < kMergePer; ++m)
         take |= (key[m] != 0ull && (want >= total_valid || (key[m] & pmask) >= prefix)) ? (1u << m) : 0u;
-    uint32_t pos = merge_scan((uint32_t)__builtin_popcount(take), wsum, &s_total);
+    uint32_t taken;
+    uint32_t pos = merge_scan((uint32_t)__builtin_popcount(take), wsum2, taken);
     int32_t *out = out_idx + (int64_t)r * k;
 #pragma unroll
     for (int m = 0; m < kMergePer; ++m)
