@@ -75,3 +75,11 @@ def test_sharded_ragged_rows_and_short_rows():
 
 def test_sharded_c3_eight_shards():
     _check(syn.make_config(3), 8)
+
+
+def test_sharded_smaller_topk():
+    # k = 1000 (G * k a multiple of 16, as the merge requires): the
+    # candidate blocks and the merge at a k other than 2048
+    n = 30000
+    p = syn.build_problem("shard_k1000", 19, [n], syn.verify_rows(0, n), topk=1000, dup_frac=0.02)
+    _check(p, 8)
