@@ -186,3 +186,19 @@ def test_1100_rows_more_than_the_zero_block_layout():
     p = syn.build_problem("rows_1100", 38, lens, rows)
     assert p.rows == 1100
     full_check(p, "rows_1100")
+
+
+def test_every_row_empty():
+    # max_bound 0: nothing is scored, every output slot is -1, and the
+    # workspace is left as it was found (zero), so a next launch is right
+    import torch
+    import fp8_key_scoring_amd as fk
+    p0 = syn.build_problem("all_empty", 39, [640], [(0, 0), (0, 0), (0, 0)])
+    assert p0.max_bound == 0
+    d = syn.device_arrays(p0, "cuda:0")
+    prob = fk._problem_from(d["q"], d["k_e4m3"], d["page_table"], 0, p0.topk, 0)
+    ws = fk.new_workspace(prob, True, "cuda:0")
+    out = fk.indexer_launch(**d, max_bound=0, topk=p0.topk, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.all(out.cpu().numpy() == -1)
+    assert not ws.any()
