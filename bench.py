@@ -6,9 +6,11 @@ call.  Inputs sit in HBM before timing starts; the timed steps rotate over
 several copies of the key pool and page table (together larger than the
 256 MB MALL) so each step streams its keys from HBM.
 
-Prints one JSON line.  Extra keys: "roofline" for the scoring kernel (timed
-per launch with HIP events on the launch stream) and "cpu_baseline" (the CPU
-oracle on a bounded sample of the same workload, on the host's cores).
+Prints one JSON line.  Extra keys: "roofline" for the launch's scoring kernel
+(timed per launch with HIP events on the launch stream, through the launch's
+scoring stage indexer_launch_score) and "cpu_baseline" (the CPU oracle on the
+same workload, or a bounded sample of it, as processes on the host's cores
+and on one core).
 """
 import argparse
 import json
@@ -66,72 +68,133 @@ def _group_max(p):
     return g
 
 
-def measured_traffic(workload):
-    """HBM bytes per scoring-kernel launch read from the committed counter
-    summary (FETCH_SIZE / WRITE_SIZE, calibrated against a plain copy), or
-    None when that summary is for another workload or the kernel sources have
-    changed since the counters were taken."""
+def source_sha256():
+    """sha256 over the HIP sources of the scoring and selection kernels: the
+    committed counter summaries carry the value they were taken on."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"pmc_score_{workload}.md")
-    if not os.path.exists(path):
-        return None
-    fields = {}
-    for line in open(path):
-        if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "score_source_sha256"):
-            k, v = line.split(":", 1)
-            fields[k] = v.strip()
     h = hashlib.sha256()
-    for fn in ("fp8_key_scoring_amd/csrc/score.hip", "fp8_key_scoring_amd/csrc/common.h"):
+    for fn in ("fp8_key_scoring_amd/csrc/score.hip", "fp8_key_scoring_amd/csrc/select.hip",
+               "fp8_key_scoring_amd/csrc/common.h"):
         with open(os.path.join(ROOT, fn), "rb") as f:
             h.update(f.read())
-    if fields.get("score_source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
-        return None
-    return int(float(fields["traffic_bytes_per_launch"]))
+    return h.hexdigest()
 
 
-def cpu_baseline(p, seconds):
-    """The oracle (scores + exact top-k) on a bounded sample of the workload,
-    sharded over host threads.  Returns the metric-unit rate."""
-    from concurrent.futures import ThreadPoolExecutor
+def profile_figures(workload):
+    """Figures read from the committed counter summary of this workload
+    (profiles/pmc_score_<workload>.md): HBM bytes per launch of the scoring
+    kernel (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy) and the
+    fraction of its time the MFMA pipes were busy.  Empty when there is no
+    summary or the kernel sources have changed since the counters were
+    taken."""
+    path = os.path.join(ROOT, "profiles", f"pmc_score_{workload}.md")
+    if not os.path.exists(path):
+        return {}
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "source_sha256", "mfma_busy_frac"):
+            k, v = line.split(":", 1)
+            fields[k] = v.strip()
+    if fields.get("source_sha256") != source_sha256():
+        return {}
+    out = {}
+    if "traffic_bytes_per_launch" in fields:
+        out["traffic"] = int(float(fields["traffic_bytes_per_launch"]))
+    if "mfma_busy_frac" in fields:
+        out["mfma_busy_frac"] = float(fields["mfma_busy_frac"])
+    return out
+
+
+def host_cpus():
+    """CPUs this process may run on: its affinity mask, capped by a cgroup
+    CPU quota when one is set."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+        if quota != "max":
+            n = min(n, max(1, int(quota) // int(period)))
+    except (OSError, ValueError):
+        pass
+    return n
+
+
+def cpu_model():
+    """The host CPU's model name (lscpu's, else /proc/cpuinfo's)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        return ""
+
+
+_CPU_PROBLEM = None   # the workload, inherited by the forked oracle workers
+
+
+def _oracle_scores(task):
     import oracle
+    r, s0, s1 = task
+    return oracle.score_range(_CPU_PROBLEM, r, s0, s1)[0]
+
+
+def cpu_baseline(p, seconds, max_procs=16):
+    """The oracle (fp64 scores + exact top-k) on the host: sharded over
+    (row, key range) as separate processes, one per available CPU (at most
+    `max_procs`, the CPU share one GPU's job gets), and on one core.  Runs
+    before anything touches the GPU (the workers are forked).  Each leg covers
+    every row of the workload, the whole of it when that is at most about
+    `seconds` of CPU work, else each row's first keys."""
+    import multiprocessing as mp
+    import oracle
+    global _CPU_PROBLEM
     oracle.build(force=False)
-    threads = max(1, min(16, os.cpu_count() or 1))
-    # calibrate: one thread, 2048 keys of row 0
+    _CPU_PROBLEM = p
     t0 = time.perf_counter()
     oracle.score_range(p, 0, 0, 2048)
     per_key = (time.perf_counter() - t0) / 2048
-    keys_per_row = int(min(p.row_bound.min(), max(4096, seconds / per_key / p.rows)))
-    keys_per_row -= keys_per_row % 1024
-    tasks = [(r, s0, min(keys_per_row, s0 + 4096)) for r in range(p.rows) for s0 in range(0, keys_per_row, 4096)]
-    t0 = time.perf_counter()
-    with ThreadPoolExecutor(threads) as ex:
-        parts = list(ex.map(lambda t: oracle.score_range(p, *t)[0], tasks))
-    rows = {}
-    for (r, s0, s1), sc in zip(tasks, parts):
-        rows.setdefault(r, []).append(sc)
-    for r in rows:
-        oracle.topk(np.concatenate(rows[r]), p.topk)
-    wall = time.perf_counter() - t0
-    n = keys_per_row * p.rows
-    # the same oracle on one core: row 0 alone, about a quarter of the CPU work
-    one_keys = int(min(p.row_bound[0], max(4096, seconds / 4 / per_key)))
-    one_keys -= one_keys % 1024
-    t0 = time.perf_counter()
-    sc1 = oracle.score_range(p, 0, 0, one_keys)[0]
-    oracle.topk(sc1, p.topk)
-    wall1 = time.perf_counter() - t0
-    model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
-    except OSError:
-        pass
-    return {"value": n / wall, "unit": "keys/s", "cores": threads, "kind": "oracle",
-            "sample": f"{p.rows} rows x first {keys_per_row} keys of the same workload: fp64 scores "
-                      f"+ exact top-{p.topk} of the sample, {threads} host threads, {wall:.2f} s",
-            "one_core": {"value": one_keys / wall1, "unit": "keys/s",
-                         "sample": f"row 0, first {one_keys} keys, one thread, {wall1:.2f} s"},
-            "cpu_model": model}
+    procs = max(1, min(max_procs, host_cpus()))
+
+    def sample(cpu_s):
+        keys = int(min(p.row_bound.max(), max(4096, cpu_s / per_key / p.rows)))
+        return keys - keys % 1024 if keys < p.row_bound.max() else keys
+
+    def run(keys_per_row, pool):
+        tasks = [(r, s0, min(int(p.row_bound[r]), keys_per_row, s0 + 16384)) for r in range(p.rows)
+                 for s0 in range(0, min(int(p.row_bound[r]), keys_per_row), 16384)]
+        t = time.perf_counter()
+        parts = pool.map(_oracle_scores, tasks, chunksize=1) if pool else [_oracle_scores(x) for x in tasks]
+        rows = {}
+        for (r, s0, s1), sc in zip(tasks, parts):
+            rows.setdefault(r, []).append(sc)
+        for r in rows:   # the selection: single-threaded per row
+            oracle.topk(np.concatenate(rows[r]), p.topk)
+        return sum(x[2] - x[1] for x in tasks), time.perf_counter() - t
+
+    k_all = sample(seconds)
+    with mp.get_context("fork").Pool(procs) as pool:
+        n_all, wall_all = run(k_all, pool)
+    k_one = sample(seconds / 2)
+    n_one, wall_one = run(k_one, None)
+    whole = k_all >= p.row_bound.max()
+    return {"value": n_all / wall_all, "unit": "keys/s", "cores": procs, "kind": "oracle",
+            "sample": (f"{'all' if whole else 'first ' + str(k_all)} keys of each of the {p.rows} rows "
+                       f"({n_all} key-rows): fp64 scores + exact top-{p.topk}, {procs} processes, "
+                       f"{wall_all:.2f} s"),
+            "one_core": {"value": n_one / wall_one, "unit": "keys/s",
+                         "sample": f"first {min(k_one, int(p.row_bound.max()))} keys of each row "
+                                   f"({n_one} key-rows), one process, {wall_one:.2f} s"},
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(), "cpus_available": host_cpus()}
 
 
 def copy_calib():
@@ -331,13 +394,16 @@ def main():
     if args.new_keys:
         new_keys_report(args)
         return
+    import synthetic as syn
+    p = syn.make_config(args.config)
+    # the CPU baseline first: its worker processes are forked before anything
+    # here has touched the GPU
+    cpu = None if args.no_cpu else cpu_baseline(p, args.cpu_seconds)
     import torch
     import fp8_key_scoring_amd as fk
-    import synthetic as syn
 
     fk.load_library()
     dev = "cuda:0"
-    p = syn.make_config(args.config)
     d = syn.device_arrays(p, dev)
     pools = [d]
     for i in range(1, args.pools):
@@ -377,16 +443,25 @@ def main():
     trial_us = sorted(marks[t].elapsed_time(marks[t + 1]) * 1e3 / (bounds[t + 1] - bounds[t])
                       for t in range(n_trials))
 
-    # hot variant: one pool (keys may stay in the MALL between launches)
+    def block_us(fn, n):
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    def hot(i):   # one pool: its keys may stay in the MALL between launches
+        fk.indexer_launch(**d, max_bound=mb, topk=p.topk, out_idx=outs, workspace=ws)
+
     for i in range(args.warmup):
-        fk.indexer_launch(**d, max_bound=mb, topk=p.topk, out_idx=outs, workspace=ws)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        fk.indexer_launch(**d, max_bound=mb, topk=p.topk, out_idx=outs, workspace=ws)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_step_hot = e0.elapsed_time(e1) / args.steps
+        hot(i)
+    ms_step_hot = block_us(hot, args.steps) * 1e-3
+    # two more rounds alternating the rotated-pool and the one-pool launches
+    n_r = max(10, args.steps // 2)
+    rounds = [{"rotated_pools": round(block_us(step, n_r), 2), "one_pool": round(block_us(hot, n_r), 2)}
+              for _ in range(2)]
 
     # the same launches replayed from a HIP graph: one graph holds a launch on
     # each key pool; replaying it back to back removes the host's per-call
@@ -418,19 +493,27 @@ def main():
     except RuntimeError as exc:   # a runtime without stream capture: report none
         print(f"graph replay not measured: {exc}", file=sys.stderr)
 
-    # scoring kernel alone: n_k back-to-back launches (rotating key pools)
-    # between two events on the launch stream; the mean is the kernel's
-    # average duration (the launches add no gaps of their own)
+    # the launch's scoring kernel: n_k back-to-back indexer_launch_score calls
+    # (the scoring stage of the timed launch, same kernel and arguments,
+    # rotating key pools) between two events on the launch stream; the mean
+    # is the kernel's average duration (the calls add no gaps of their own).
+    # The passes add their digit counts together, so the workspace is
+    # restored afterwards.
     n_k = max(20, min(args.steps, 200))
+    ws_t = fk.new_workspace(prob, True, dev)
+
+    def score_stage(i):
+        fk.indexer_launch_score(**pools[i % len(pools)], max_bound=mb, topk=p.topk, workspace=ws_t)
+
+    for i in range(args.warmup):
+        score_stage(i)
+    score_ms = block_us(score_stage, n_k) * 1e-3
+    fk.workspace_init(ws_t)
+    # indexer_score's kernel (scores only, no digit counts), for comparison
     for i in range(args.warmup):
         fk.indexer_score(**pools[i % len(pools)], max_bound=mb, scores=scores)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(n_k):
-        fk.indexer_score(**pools[i % len(pools)], max_bound=mb, scores=scores)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    score_ms = e0.elapsed_time(e1) / n_k
+    score_only_us = block_us(lambda i: fk.indexer_score(**pools[i % len(pools)], max_bound=mb, scores=scores),
+                             n_k)
 
     key_rows = p.key_rows()
     flops = FLOP_PER_KEY_ROW * key_rows
@@ -438,17 +521,20 @@ def main():
     ach_tflops = flops / (score_ms * 1e-3) / 1e12
     ach_gbs = abytes / (score_ms * 1e-3) / 1e9
     mfma_bound = flops / (PEAK_BF16_TFLOPS * 1e12) >= abytes / (PEAK_HBM_GBS * 1e9)
-    traffic = measured_traffic(p.name)
+    prof = profile_figures(p.name)
+    traffic = prof.get("traffic")
     roof = ({"bound": "mfma", "achieved": round(ach_tflops, 2), "peak": PEAK_BF16_TFLOPS,
              "unit": "TFLOP/s", "frac": round(ach_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
             if mfma_bound else
             {"bound": "hbm", "achieved": round(ach_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
              "frac": round(ach_gbs / PEAK_HBM_GBS, 4), "traffic": traffic})
-    roof.update({"kernel": "score_kernel<false> (what indexer_score launches; indexer_launch runs the "
-                           "same kernel with the first-digit count fused in)",
+    roof.update({"kernel": "the scoring kernel of indexer_launch (with the selection's digit counts), "
+                           "timed through indexer_launch_score",
                  "kernel_us": round(score_ms * 1e3, 2), "traffic_unit": "bytes per launch",
                  "algorithmic_flops": flops, "algorithmic_bytes": abytes,
-                 "hbm_gbs_at_kernel_time": round(ach_gbs, 1)})
+                 "hbm_gbs_at_kernel_time": round(ach_gbs, 1),
+                 "mfma_busy_frac": prof.get("mfma_busy_frac"),
+                 "score_only_kernel_us": round(score_only_us, 2)})
     peaks = measured_peaks(torch, dev)
     mpeak = peaks["bf16_mfma_TFLOPs"] if mfma_bound else peaks["hbm_read_GBs"]
     roof.update({"measured_peak": mpeak, "frac_of_measured_peak": round(roof["achieved"] / mpeak, 4),
@@ -467,7 +553,9 @@ def main():
         "us_per_launch_hot": ms_step_hot * 1e3,
         "us_per_launch_graph": None if us_graph is None else round(us_graph, 2),
         "us_per_launch_trials": {"n": n_trials, "median": round(trial_us[n_trials // 2], 2),
-                                 "min": round(trial_us[0], 2), "max": round(trial_us[-1], 2)},
+                                 "min": round(trial_us[0], 2), "max": round(trial_us[-1], 2),
+                                 "over_1.1x_median": sum(t > 1.1 * trial_us[n_trials // 2] for t in trial_us)},
+        "us_per_launch_rounds": rounds,
         "launch_roofline_frac": round(step_roof_s / (ms_step * 1e-3), 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -479,8 +567,8 @@ def main():
                    "pools_rotated": len(pools)},
         "roofline": roof,
     }
-    if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res))
 
 

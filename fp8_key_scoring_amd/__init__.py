@@ -22,6 +22,7 @@ MAX_TOPK = 2048
 
 EXPORTED = ("fp8idx_abi_version", "fp8idx_strerror", "fp8idx_workspace_size",
             "fp8idx_workspace_init", "indexer_score", "indexer_topk", "indexer_launch",
+            "indexer_launch_score", "indexer_launch_select",
             "indexer_shard_candidates", "indexer_merge_topk", "indexer_write_keys",
             "indexer_launch_new_keys", "indexer_validate")
 
@@ -72,6 +73,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.indexer_launch.restype = ctypes.c_int
     lib.indexer_launch.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, P, P,
                                    ctypes.c_size_t, P]
+    lib.indexer_launch_score.restype = ctypes.c_int
+    lib.indexer_launch_score.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, P,
+                                         ctypes.c_size_t, P]
+    lib.indexer_launch_select.restype = ctypes.c_int
+    lib.indexer_launch_select.argtypes = [ctypes.POINTER(Problem), P, P, P, P, ctypes.c_size_t, P]
     lib.indexer_validate.restype = ctypes.c_int
     lib.indexer_validate.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P]
     lib.indexer_write_keys.restype = ctypes.c_int
@@ -130,6 +136,12 @@ def new_workspace(prob: Problem, scores_in_workspace: bool, device):
     return ws
 
 
+
+def workspace_init(ws) -> None:
+    """Zero-fills a workspace tensor on its device's current stream (restores
+    one whose counters a misuse left non-zero)."""
+    _check(load_library().fp8idx_workspace_init(ws.data_ptr(), ws.numel(), _stream(ws.device)))
+
 def _problem_from(q, k_e4m3, page_table, max_bound: int, topk: int, score_stride: int) -> Problem:
     return make_problem(rows=q.shape[0], num_pages=k_e4m3.shape[0], pt_rows=page_table.shape[0],
                         pt_stride=page_table.shape[1], max_bound=max_bound, topk=topk,
@@ -148,6 +160,26 @@ def _check_inputs(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound):
     assert row_bound.dtype == torch.int32 and tuple(row_bound.shape) == (R,) and row_bound.is_contiguous()
 
 
+def _check_scores(scores, rows: int, max_bound: int, device) -> None:
+    """scores must be an fp32 [>= rows, >= max_bound] matrix with unit inner
+    stride on the inputs' device: the kernels write row r at scores + r *
+    stride(0) for every key below the row's bound."""
+    import torch
+    assert scores.dtype == torch.float32, "scores must be float32"
+    assert scores.dim() == 2 and scores.stride(1) == 1, "scores must be 2-D with unit inner stride"
+    assert scores.shape[0] >= rows and scores.shape[1] >= max_bound, \
+        f"scores {tuple(scores.shape)} too small for {rows} rows x {max_bound} keys"
+    assert scores.device == torch.device(device), "scores must be on the inputs' device"
+
+
+def _check_out(out_idx, rows: int, topk: int, device) -> None:
+    """out_idx must be a contiguous int32 [rows, topk] tensor on the inputs' device."""
+    import torch
+    assert out_idx.dtype == torch.int32 and out_idx.is_contiguous(), "out_idx must be contiguous int32"
+    assert tuple(out_idx.shape) == (rows, topk), f"out_idx must be ({rows}, {topk}), got {tuple(out_idx.shape)}"
+    assert out_idx.device == torch.device(device), "out_idx must be on the inputs' device"
+
+
 def indexer_score(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound, *, max_bound: int,
                   scores=None):
     """Scores [rows, score_stride] fp32; entries at or past a row's bound untouched."""
@@ -156,7 +188,7 @@ def indexer_score(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound, *, max_b
     if scores is None:
         scores = torch.full((q.shape[0], max(1, max_bound)), float("nan"), dtype=torch.float32,
                             device=q.device)
-    assert scores.dtype == torch.float32 and scores.dim() == 2 and scores.stride(1) == 1
+    _check_scores(scores, q.shape[0], max_bound, q.device)
     prob = _problem_from(q, k_e4m3, page_table, max_bound, MAX_TOPK, scores.stride(0))
     _check(load_library().indexer_score(ctypes.byref(prob), _ptr(q), _ptr(w), _ptr(k_e4m3),
                                         _ptr(k_scale), _ptr(page_table), _ptr(row_pt),
@@ -168,12 +200,15 @@ def indexer_topk(scores, row_bound, *, max_bound: int, topk: int = MAX_TOPK, out
                  workspace=None):
     """Exact top-k indices [rows, topk] int32 (ascending index order, -1 padded)."""
     import torch
-    assert scores.dtype == torch.float32 and scores.dim() == 2 and scores.stride(1) == 1
-    R = scores.shape[0]
+    R = row_bound.shape[0]
+    assert row_bound.dtype == torch.int32 and row_bound.is_contiguous()
+    _check_scores(scores, R, max_bound, scores.device)
+    assert row_bound.device == scores.device, "row_bound must be on the scores' device"
     prob = make_problem(rows=R, num_pages=1, pt_rows=1, pt_stride=max(1, (max_bound + 63) // 64),
                         max_bound=max_bound, topk=topk, score_stride=scores.stride(0))
     if out_idx is None:
         out_idx = torch.empty((R, topk), dtype=torch.int32, device=scores.device)
+    _check_out(out_idx, R, topk, scores.device)
     if workspace is None:
         workspace = new_workspace(prob, False, scores.device)
     _check(load_library().indexer_topk(ctypes.byref(prob), _ptr(scores), _ptr(row_bound),
@@ -188,10 +223,13 @@ def indexer_launch(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound, *, max_
     import torch
     _check_inputs(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound)
     R = q.shape[0]
+    if scores is not None:
+        _check_scores(scores, R, max_bound, q.device)
     sstride = scores.stride(0) if scores is not None else 0
     prob = _problem_from(q, k_e4m3, page_table, max_bound, topk, sstride)
     if out_idx is None:
         out_idx = torch.empty((R, topk), dtype=torch.int32, device=q.device)
+    _check_out(out_idx, R, topk, q.device)
     if workspace is None:
         workspace = new_workspace(prob, scores is None, q.device)
     _check(load_library().indexer_launch(ctypes.byref(prob), _ptr(q), _ptr(w), _ptr(k_e4m3),
@@ -200,6 +238,46 @@ def indexer_launch(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound, *, max_
                                          _ptr(workspace), workspace.numel(), _stream(q.device)))
     return out_idx
 
+
+
+def indexer_launch_score(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound, *, max_bound: int,
+                         topk: int = MAX_TOPK, scores=None, workspace):
+    """The scoring stage of indexer_launch: scores (into the workspace when
+    `scores` is None) and the selection's digit counts added into the
+    workspace.  Exactly one indexer_launch_select with the same arguments
+    must follow before the workspace is used again."""
+    _check_inputs(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound)
+    R = q.shape[0]
+    if scores is not None:
+        _check_scores(scores, R, max_bound, q.device)
+    sstride = scores.stride(0) if scores is not None else 0
+    prob = _problem_from(q, k_e4m3, page_table, max_bound, topk, sstride)
+    _check(load_library().indexer_launch_score(ctypes.byref(prob), _ptr(q), _ptr(w), _ptr(k_e4m3),
+                                               _ptr(k_scale), _ptr(page_table), _ptr(row_pt),
+                                               _ptr(row_bound), _ptr(scores), _ptr(workspace),
+                                               workspace.numel(), _stream(q.device)))
+
+
+def indexer_launch_select(row_bound, *, max_bound: int, topk: int = MAX_TOPK, scores=None, out_idx=None,
+                          workspace, rows: Optional[int] = None):
+    """The selection stage of indexer_launch, from the scores and counts an
+    indexer_launch_score call left (same scores tensor or None, same
+    workspace).  Returns out_idx [rows, topk] int32."""
+    import torch
+    R = row_bound.shape[0] if rows is None else rows
+    assert row_bound.dtype == torch.int32 and tuple(row_bound.shape) == (R,) and row_bound.is_contiguous()
+    if scores is not None:
+        _check_scores(scores, R, max_bound, row_bound.device)
+    if out_idx is None:
+        out_idx = torch.empty((R, topk), dtype=torch.int32, device=row_bound.device)
+    _check_out(out_idx, R, topk, row_bound.device)
+    prob = make_problem(rows=R, num_pages=1, pt_rows=1, pt_stride=max(1, (max_bound + 63) // 64),
+                        max_bound=max_bound, topk=topk,
+                        score_stride=scores.stride(0) if scores is not None else 0)
+    _check(load_library().indexer_launch_select(ctypes.byref(prob), _ptr(scores), _ptr(row_bound),
+                                                _ptr(out_idx), _ptr(workspace), workspace.numel(),
+                                                _stream(row_bound.device)))
+    return out_idx
 
 VALID_BOUND, VALID_ROW_PT, VALID_PAGE = 1, 2, 4
 
@@ -256,10 +334,13 @@ def indexer_launch_new_keys(q, w, k_new, k_e4m3, k_scale, page_table, row_pt, ro
     _check_inputs(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound)
     R = q.shape[0]
     _check_new_keys(k_new, R)
+    if scores is not None:
+        _check_scores(scores, R, max_bound, q.device)
     sstride = scores.stride(0) if scores is not None else 0
     prob = _problem_from(q, k_e4m3, page_table, max_bound, topk, sstride)
     if out_idx is None:
         out_idx = torch.empty((R, topk), dtype=torch.int32, device=q.device)
+    _check_out(out_idx, R, topk, q.device)
     if workspace is None:
         workspace = new_workspace(prob, scores is None, q.device)
     _check(load_library().indexer_launch_new_keys(ctypes.byref(prob), _ptr(q), _ptr(w), _ptr(k_new),

@@ -107,6 +107,39 @@ int run_select(const fp8idx_problem_t *p, const float *scores, int64_t sstride,
     return to_code(launch_finalize(a, st));
 }
 
+constexpr int kStageScore = 1, kStageSelect = 2;
+
+// Scoring with the selection's digit counts into the workspace (kStageScore)
+// and/or the selection from those counts (kStageSelect); every check before
+// anything is enqueued.  zero_rows: the workspace's zero-block layout (0 for
+// a caller's workspace).
+int launch_checked(const fp8idx_problem_t *p, const void *q_bf16, const float *w, const uint8_t *k_e4m3,
+                   const float *k_scale, const int32_t *page_table, const int32_t *row_pt,
+                   const int32_t *row_bound, float *scores, int32_t *out_idx, void *ws, size_t ws_bytes,
+                   int zero_rows, int stages, hipStream_t st) {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    rc = check_score_inputs(p, q_bf16, w, k_e4m3, k_scale, page_table, row_pt, row_bound);
+    if (rc) return rc;
+    if ((stages & kStageSelect) && (!out_idx || !aligned(out_idx, 4))) return FP8IDX_EINVAL;
+    if (scores && (!aligned(scores, 4) || p->score_stride < p->max_bound)) return FP8IDX_EINVAL;
+    const WsLayout L = ws_layout(p->rows, p->max_bound, scores == nullptr, zero_rows);
+    if (!ws || !aligned(ws, 256) || ws_bytes < L.total) return FP8IDX_EWORKSPACE;
+    rc = check_device();
+    if (rc) return rc;
+    unsigned char *wsb = (unsigned char *)ws;
+    float *sc = scores ? scores : (float *)(wsb + L.scores);
+    const int64_t sstride = scores ? p->score_stride : L.sstride;
+    if (stages & kStageScore) {
+        ScoreArgs a = make_score_args(p, q_bf16, w, k_e4m3, k_scale, page_table, row_pt, row_bound,
+                                      sc, sstride, (uint32_t *)(wsb + L.hist1));
+        rc = to_code(launch_score(a, st));
+        if (rc) return rc;
+    }
+    if (stages & kStageSelect) return run_select(p, sc, sstride, row_bound, out_idx, wsb, L, false, st);
+    return FP8IDX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -174,25 +207,32 @@ int indexer_launch(const fp8idx_problem_t *p, const void *q_bf16, const float *w
                    const uint8_t *k_e4m3, const float *k_scale, const int32_t *page_table,
                    const int32_t *row_pt, const int32_t *row_bound, float *scores,
                    int32_t *out_idx, void *ws, size_t ws_bytes, void *stream) {
+    return launch_checked(p, q_bf16, w, k_e4m3, k_scale, page_table, row_pt, row_bound, scores, out_idx, ws,
+                          ws_bytes, 0, kStageScore | kStageSelect, (hipStream_t)stream);
+}
+
+int indexer_launch_score(const fp8idx_problem_t *p, const void *q_bf16, const float *w,
+                         const uint8_t *k_e4m3, const float *k_scale, const int32_t *page_table,
+                         const int32_t *row_pt, const int32_t *row_bound, float *scores,
+                         void *ws, size_t ws_bytes, void *stream) {
+    return launch_checked(p, q_bf16, w, k_e4m3, k_scale, page_table, row_pt, row_bound, scores, nullptr, ws,
+                          ws_bytes, 0, kStageScore, (hipStream_t)stream);
+}
+
+int indexer_launch_select(const fp8idx_problem_t *p, const float *scores, const int32_t *row_bound,
+                          int32_t *out_idx, void *ws, size_t ws_bytes, void *stream) {
     int rc = check_problem(p);
     if (rc) return rc;
-    rc = check_score_inputs(p, q_bf16, w, k_e4m3, k_scale, page_table, row_pt, row_bound);
-    if (rc) return rc;
-    if (!out_idx || !aligned(out_idx, 4)) return FP8IDX_EINVAL;
+    if (!row_bound || !aligned(row_bound, 4) || !out_idx || !aligned(out_idx, 4)) return FP8IDX_EINVAL;
     if (scores && (!aligned(scores, 4) || p->score_stride < p->max_bound)) return FP8IDX_EINVAL;
     const WsLayout L = ws_layout(p->rows, p->max_bound, scores == nullptr);
     if (!ws || !aligned(ws, 256) || ws_bytes < L.total) return FP8IDX_EWORKSPACE;
     rc = check_device();
     if (rc) return rc;
     unsigned char *wsb = (unsigned char *)ws;
-    float *sc = scores ? scores : (float *)(wsb + L.scores);
+    const float *sc = scores ? scores : (const float *)(wsb + L.scores);
     const int64_t sstride = scores ? p->score_stride : L.sstride;
-    hipStream_t st = (hipStream_t)stream;
-    ScoreArgs a = make_score_args(p, q_bf16, w, k_e4m3, k_scale, page_table, row_pt, row_bound,
-                                  sc, sstride, (uint32_t *)(wsb + L.hist1));
-    rc = to_code(launch_score(a, st));
-    if (rc) return rc;
-    return run_select(p, sc, sstride, row_bound, out_idx, wsb, L, false, st);
+    return run_select(p, sc, sstride, row_bound, out_idx, wsb, L, false, (hipStream_t)stream);
 }
 
 int indexer_validate(const fp8idx_problem_t *p, const int32_t *page_table, const int32_t *row_pt,

@@ -85,7 +85,10 @@ struct WsLayout {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-inline WsLayout ws_layout(int rows, int max_bound, bool own_scores) {
+// zero_rows: rows the zero block is laid out for; 0 means max(rows,
+// kZeroRows) (a caller's workspace), a fixed value gives every problem of up
+// to that many rows the same zero block (the library's static scratch).
+inline WsLayout ws_layout(int rows, int max_bound, bool own_scores, int zero_rows = 0) {
     WsLayout L{};
     const int64_t mb = max_bound > 0 ? max_bound : 1;
     int n = (int)((mb + kSelTile - 1) / kSelTile);
@@ -97,7 +100,7 @@ inline WsLayout ws_layout(int rows, int max_bound, bool own_scores) {
     L.sstride = (int64_t)align_up((size_t)mb, 64);
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
-    const size_t rz = (size_t)(rows > kZeroRows ? rows : kZeroRows);
+    const size_t rz = zero_rows > 0 ? (size_t)zero_rows : (size_t)(rows > kZeroRows ? rows : kZeroRows);
     L.hist1 = take(rz * kHist1Slots * kBins1 * 4);
     L.hist2 = take(rz * kHist2Slots * kBins2 * 4);
     L.hist3 = take(rz * kBins3 * 4);

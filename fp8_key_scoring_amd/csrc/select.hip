@@ -481,7 +481,10 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
         if (wave == 0) {
             const uint32_t c = live ? ne : 0u, cc = live ? ncx : 0u;
             const uint32_t rm = c > 16u * kPre ? c - 16u * kPre : 0u;
-            const uint64_t big = __ballot(cc > (uint32_t)kCandSlice);
+            // a slice holding more entries than its capacity (possible only
+            // with counters left dirty by a misused workspace) is never read
+            // past its end: the row takes the fallback instead
+            const uint64_t big = __ballot(cc > (uint32_t)kCandSlice || c > (uint32_t)kSliceCap);
             uint32_t incl = c, cincl = cc, rincl = rm;
             for (int o = 1; o < 64; o <<= 1) {
                 const uint32_t v = __shfl_up(incl, o), w = __shfl_up(cincl, o), z = __shfl_up(rincl, o);

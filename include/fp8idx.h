@@ -144,6 +144,39 @@ int indexer_launch(const fp8idx_problem_t *p,
                    float *scores, int32_t *out_idx,
                    void *ws, size_t ws_bytes, void *stream);
 
+/* The two stages of indexer_launch as separate calls (indexer_launch is
+ * exactly indexer_launch_score followed by indexer_launch_select on one
+ * stream and workspace).  For callers that put work between the stages or
+ * time them apart.
+ *
+ * indexer_launch_score: the scoring pass of the fused launch (the same page,
+ * Motivation and Modifications rows 1-2 for the scoring; row 4 for counting
+ * the selection's first radix digit while scoring): scores as indexer_score
+ * writes them (into the workspace when `scores` is NULL) and the per-row
+ * radix-digit counts the selection reads, added into the workspace's zero
+ * block.  Arguments as for indexer_launch without out_idx.
+ *
+ * indexer_launch_select: the selection from those scores and counts: out_idx
+ * as for indexer_topk; the counts are consumed and the zero block left zero.
+ * `scores` must be the pointer (or NULL, for scores in the workspace) and
+ * p->score_stride the stride given to indexer_launch_score; p, row_bound and
+ * the workspace must be the same.
+ *
+ * Exactly one indexer_launch_select must follow each indexer_launch_score on
+ * a workspace before the workspace is used again (two scoring passes in a row
+ * add their counts together; fp8idx_workspace_init restores a workspace).
+ * Errors as for indexer_launch. */
+int indexer_launch_score(const fp8idx_problem_t *p,
+                         const void *q_bf16, const float *w,
+                         const uint8_t *k_e4m3, const float *k_scale,
+                         const int32_t *page_table, const int32_t *row_pt,
+                         const int32_t *row_bound,
+                         float *scores, void *ws, size_t ws_bytes, void *stream);
+
+int indexer_launch_select(const fp8idx_problem_t *p,
+                          const float *scores, const int32_t *row_bound,
+                          int32_t *out_idx, void *ws, size_t ws_bytes, void *stream);
+
 /* Checks the device arrays the calls above trust and writes a status word to
  * `status` (one device uint32, 4-byte aligned; zeroed by this call first, then
  * OR-ed): bit 0 (1) some row_bound outside [0, max_bound]; bit 1 (2) some

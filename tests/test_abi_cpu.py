@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     for n in ("indexer_score", "indexer_topk", "indexer_launch", "fp8idx_workspace_size",
               "fp8idx_workspace_init", "fp8idx_abi_version", "fp8idx_strerror",
               "indexer_shard_candidates", "indexer_merge_topk", "indexer_write_keys",
-              "indexer_launch_new_keys", "indexer_validate"):
+              "indexer_launch_new_keys", "indexer_validate", "indexer_launch_score",
+              "indexer_launch_select"):
         assert n in names
 
 
@@ -96,6 +97,34 @@ def test_host_side_argument_errors(lib):
     assert lib.fp8idx_workspace_init(None, 256, None) == -1
     assert lib.fp8idx_workspace_init(0x100001, 256, None) == -1
 
+
+
+def test_launch_stage_argument_errors(lib):
+    """indexer_launch_score / indexer_launch_select reject bad arguments on the host."""
+    import fp8_key_scoring_amd as fk
+    good = [0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000]   # q .. row_bound, never dereferenced
+    p = fk.make_problem(rows=4, num_pages=16, pt_rows=1, pt_stride=16, max_bound=1024, topk=2048,
+                        score_stride=1024)
+    ws_need = fk.workspace_size(p, False)
+    for i in range(len(good)):
+        ptrs = list(good)
+        ptrs[i] = None
+        assert lib.indexer_launch_score(ctypes.byref(p), *ptrs, 0x9000, 0x100000, 1 << 30, None) == -1
+    # workspace missing, too small, misaligned
+    assert lib.indexer_launch_score(ctypes.byref(p), *good, 0x9000, None, 1 << 30, None) == -2
+    assert lib.indexer_launch_score(ctypes.byref(p), *good, 0x9000, 0x100000, ws_need - 4, None) == -2
+    assert lib.indexer_launch_score(ctypes.byref(p), *good, 0x9000, 0x100010, 1 << 30, None) == -2
+    # scores given with a stride below max_bound
+    p2 = fk.make_problem(rows=4, num_pages=16, pt_rows=1, pt_stride=16, max_bound=1024, topk=2048,
+                         score_stride=1000)
+    assert lib.indexer_launch_score(ctypes.byref(p2), *good, 0x9000, 0x100000, 1 << 30, None) == -1
+    # select: out_idx and row_bound required; the workspace as for the launch
+    assert lib.indexer_launch_select(ctypes.byref(p), 0x9000, 0x7000, None, 0x100000, 1 << 30, None) == -1
+    assert lib.indexer_launch_select(ctypes.byref(p), 0x9000, None, 0xA000, 0x100000, 1 << 30, None) == -1
+    assert lib.indexer_launch_select(ctypes.byref(p), 0x9000, 0x7000, 0xA000, 0x100000, ws_need - 4, None) == -2
+    # without caller scores the workspace must also hold them
+    ws_own = fk.workspace_size(p, True)
+    assert lib.indexer_launch_select(ctypes.byref(p), None, 0x7000, 0xA000, 0x100000, ws_own - 4, None) == -2
 
 def test_sharded_selection_argument_errors(lib):
     """Host-side checks of the key-sharded calls (nothing is launched: every

@@ -39,6 +39,28 @@ def test_launch_equals_score_then_topk():
     assert np.array_equal(o1, o2.cpu().numpy())
 
 
+
+def test_launch_equals_its_two_stages():
+    # indexer_launch_score then indexer_launch_select, with caller scores and
+    # with scores in the workspace, twice in a row on one workspace
+    p = _prob(25)
+    say("[gpu] launch vs its two stages")
+    s1, o1 = run_launch(p)
+    d = to_device(p)
+    mb = p.max_bound
+    for own in (False, True):
+        prob = fk._problem_from(d["q"], d["k_e4m3"], d["page_table"], mb, p.topk, 0)
+        ws = fk.new_workspace(prob, own, "cuda:0")
+        for rep in range(2):
+            sc = None if own else torch.full((p.rows, mb), float("nan"), dtype=torch.float32, device="cuda:0")
+            fk.indexer_launch_score(**d, max_bound=mb, topk=p.topk, scores=sc, workspace=ws)
+            o2 = fk.indexer_launch_select(d["row_bound"], max_bound=mb, topk=p.topk, scores=sc, workspace=ws)
+            torch.cuda.synchronize()
+            if sc is not None:
+                assert np.array_equal(s1.view(np.uint32), sc.cpu().numpy().view(np.uint32))
+            assert np.array_equal(o1, o2.cpu().numpy()), (own, rep)
+        assert not ws[:_zero_block_bytes(p.rows)].any(), "counters left non-zero"
+
 def test_scores_in_workspace():
     p = _prob(23)
     say("[gpu] scores kept in the workspace")

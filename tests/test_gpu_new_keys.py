@@ -164,3 +164,12 @@ def test_write_hand_worked_cases():
             want[int(i)] = int(c, 16)
         assert np.array_equal(k8[page, pos % 64], want), case["name"]
         assert int(ks[page, pos % 64:pos % 64 + 1].view(np.uint32)[0]) == int(case["scale_bits"], 16), case["name"]
+
+
+def test_write_hand_worked_positions():
+    # the literal positions of tests/golden/new_key_positions.json, written by the GPU
+    from golden_cases import check_new_key_positions, new_key_positions
+    p, kn, want = new_key_positions()
+    say(f"[gpu] new-key write, hand-worked positions: rows={p.rows}")
+    k8, ks = _write_on_gpu(p, kn)
+    check_new_key_positions(k8, ks, want, p.k_e4m3, p.k_scale)

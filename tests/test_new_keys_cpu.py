@@ -132,3 +132,14 @@ def test_hand_worked_quantizations(oracle_lib):
         for i, c in case["codes"].items():
             want[int(i)] = int(c, 16)
         assert np.array_equal(codes, want), case["name"]
+
+
+def test_hand_worked_positions(oracle_lib):
+    """tests/golden/new_key_positions.json: literal (page, slot) positions of
+    the new keys for bounds 1, 64, 65, 128, 130 and 100 over a hand-written
+    page table, and three rows that write nothing (bound 0, a page id of -1,
+    a page-table row that does not exist)."""
+    from golden_cases import check_new_key_positions, new_key_positions
+    p, kn, want = new_key_positions()
+    k8, ks = oracle_lib.write_new_keys(p, kn)
+    check_new_key_positions(k8, ks, want, p.k_e4m3, p.k_scale)
