@@ -22,7 +22,7 @@ MAX_TOPK = 2048
 
 EXPORTED = ("fp8idx_abi_version", "fp8idx_strerror", "fp8idx_workspace_size",
             "fp8idx_workspace_init", "indexer_score", "indexer_topk", "indexer_launch",
-            "indexer_launch_score", "indexer_launch_select",
+            "indexer_launch_score", "indexer_launch_select", "indexer_launch_static",
             "indexer_shard_candidates", "indexer_merge_topk", "indexer_write_keys",
             "indexer_launch_new_keys", "indexer_validate")
 
@@ -78,6 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          ctypes.c_size_t, P]
     lib.indexer_launch_select.restype = ctypes.c_int
     lib.indexer_launch_select.argtypes = [ctypes.POINTER(Problem), P, P, P, P, ctypes.c_size_t, P]
+    lib.indexer_launch_static.restype = ctypes.c_int
+    lib.indexer_launch_static.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, P, P]
     lib.indexer_validate.restype = ctypes.c_int
     lib.indexer_validate.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P]
     lib.indexer_write_keys.restype = ctypes.c_int
@@ -277,6 +279,33 @@ def indexer_launch_select(row_bound, *, max_bound: int, topk: int = MAX_TOPK, sc
     _check(load_library().indexer_launch_select(ctypes.byref(prob), _ptr(scores), _ptr(row_bound),
                                                 _ptr(out_idx), _ptr(workspace), workspace.numel(),
                                                 _stream(row_bound.device)))
+    return out_idx
+
+
+STATIC_MAX_ROWS = 256
+STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def indexer_launch_static(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound, *, max_bound: int,
+                          topk: int = MAX_TOPK, scores=None, out_idx=None):
+    """indexer_launch on the library's static per-GPU scratch (no workspace;
+    the C call allocates nothing).  Pass `out_idx` (and `scores`) to allocate
+    nothing here either.  Calls that may overlap on one GPU race.  Returns
+    out_idx [rows, topk] int32."""
+    import torch
+    _check_inputs(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound)
+    R = q.shape[0]
+    if scores is not None:
+        _check_scores(scores, R, max_bound, q.device)
+    sstride = scores.stride(0) if scores is not None else 0
+    prob = _problem_from(q, k_e4m3, page_table, max_bound, topk, sstride)
+    if out_idx is None:
+        out_idx = torch.empty((R, topk), dtype=torch.int32, device=q.device)
+    _check_out(out_idx, R, topk, q.device)
+    _check(load_library().indexer_launch_static(ctypes.byref(prob), _ptr(q), _ptr(w), _ptr(k_e4m3),
+                                                _ptr(k_scale), _ptr(page_table), _ptr(row_pt),
+                                                _ptr(row_bound), _ptr(scores), _ptr(out_idx),
+                                                _stream(q.device)))
     return out_idx
 
 VALID_BOUND, VALID_ROW_PT, VALID_PAGE = 1, 2, 4

@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 using namespace fp8idx;
 
@@ -153,6 +154,7 @@ const char *fp8idx_strerror(int code) {
     case FP8IDX_EWORKSPACE: return "workspace missing or too small";
     case FP8IDX_ELAUNCH: return "kernel launch failed";
     case FP8IDX_EDEVICE: return "no gfx950 device is current";
+    case FP8IDX_ESCRATCH: return "problem larger than the static scratch of indexer_launch_static";
     default: return "unknown error";
     }
 }
@@ -233,6 +235,58 @@ int indexer_launch_select(const fp8idx_problem_t *p, const float *scores, const 
     const float *sc = scores ? scores : (const float *)(wsb + L.scores);
     const int64_t sstride = scores ? p->score_stride : L.sstride;
     return run_select(p, sc, sstride, row_bound, out_idx, wsb, L, false, (hipStream_t)stream);
+}
+
+// ---- The launch with the library's own scratch in place of a workspace.
+// scratch: file-scope device memory, one copy per GPU the library runs on
+// (the runtime places it when the code object is loaded and keeps it until
+// the process ends).  Its host-side name is not a device address: host code
+// uses only the per-device address hipGetSymbolAddress returns.
+constexpr size_t kScratchBytes = (size_t)FP8IDX_STATIC_SCRATCH_BYTES;
+constexpr int kScratchRows = FP8IDX_STATIC_MAX_ROWS;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+unsigned char *g_scratch_ptr[64];   // per device: the scratch's device address (null: not set up)
+bool g_scratch_dirty[64];           // per device: a call failed after enqueueing work; clear again
+}  // namespace
+
+int indexer_launch_static(const fp8idx_problem_t *p, const void *q_bf16, const float *w,
+                          const uint8_t *k_e4m3, const float *k_scale, const int32_t *page_table,
+                          const int32_t *row_pt, const int32_t *row_bound, float *scores,
+                          int32_t *out_idx, void *stream) {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if (p->rows > kScratchRows) return FP8IDX_ESCRATCH;
+    if (ws_layout(p->rows, p->max_bound, scores == nullptr, kScratchRows).total > kScratchBytes)
+        return FP8IDX_ESCRATCH;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return FP8IDX_EDEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    unsigned char *ws = g_scratch_ptr[dev];
+    const size_t zero_bytes = ws_layout(1, 1, false, kScratchRows).state;
+    if (!ws) {
+        // set-up, once per device with that device current: the scratch's
+        // address on this device, and its zero block cleared (a fill
+        // kernel) ahead of the first launch on the caller's stream
+        rc = check_device();
+        if (rc) return rc;
+        void *addr = nullptr;
+        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return FP8IDX_ELAUNCH;
+        g_scratch_ptr[dev] = ws = (unsigned char *)addr;
+        g_scratch_dirty[dev] = true;
+    }
+    if (g_scratch_dirty[dev]) {
+        if (launch_fill_zero(ws, zero_bytes, (hipStream_t)stream) != hipSuccess) return FP8IDX_ELAUNCH;
+        g_scratch_dirty[dev] = false;
+    }
+    rc = launch_checked(p, q_bf16, w, k_e4m3, k_scale, page_table, row_pt, row_bound, scores, out_idx, ws,
+                        kScratchBytes, kScratchRows, kStageScore | kStageSelect, (hipStream_t)stream);
+    // a launch error after the scoring pass was enqueued can leave counts in
+    // the zero block: the next call clears it first
+    if (rc == FP8IDX_ELAUNCH) g_scratch_dirty[dev] = true;
+    return rc;
 }
 
 int indexer_validate(const fp8idx_problem_t *p, const int32_t *page_table, const int32_t *row_pt,

@@ -65,13 +65,18 @@ extern "C" {
 #define FP8IDX_HEAD_DIM 128
 #define FP8IDX_PAGE 64
 #define FP8IDX_MAX_TOPK 2048
+/* Limits of indexer_launch_static's scratch (one per GPU): at most this many
+ * rows, and a workspace layout of at most this many bytes. */
+#define FP8IDX_STATIC_MAX_ROWS 256
+#define FP8IDX_STATIC_SCRATCH_BYTES (64u << 20)
 
 enum {
     FP8IDX_OK = 0,
     FP8IDX_EINVAL = -1,     /* invalid argument (null pointer, size, alignment) */
     FP8IDX_EWORKSPACE = -2, /* workspace null or smaller than fp8idx_workspace_size */
     FP8IDX_ELAUNCH = -3,    /* the HIP runtime reported an error for a launch */
-    FP8IDX_EDEVICE = -4     /* current device is not gfx950 / no device */
+    FP8IDX_EDEVICE = -4,    /* current device is not gfx950 / no device */
+    FP8IDX_ESCRATCH = -5    /* problem larger than indexer_launch_static's scratch */
 };
 
 /* Problem descriptor (plain data, passed by host pointer).
@@ -176,6 +181,29 @@ int indexer_launch_score(const fp8idx_problem_t *p,
 int indexer_launch_select(const fp8idx_problem_t *p,
                           const float *scores, const int32_t *row_bound,
                           int32_t *out_idx, void *ws, size_t ws_bytes, void *stream);
+
+/* indexer_launch without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors as
+ * indexer_launch; the workspace is the library's own static scratch of
+ * FP8IDX_STATIC_SCRATCH_BYTES (64 MiB) of device memory per GPU, held by each
+ * GPU the library runs on until the process ends.  The call allocates
+ * nothing.  Its first call on a GPU looks up that GPU's scratch and clears
+ * its counters with a fill kernel on `stream`; every call leaves them clear.
+ *
+ * Limits: p->rows <= FP8IDX_STATIC_MAX_ROWS and the workspace the problem
+ * needs (fp8idx_workspace_size, with the counters laid out for 256 rows; with
+ * scores == NULL the scores live there too) at most 64 MiB; a larger problem
+ * returns FP8IDX_ESCRATCH before anything is enqueued.  All calls on one GPU
+ * share its scratch: calls that may overlap on the GPU (on different streams
+ * without ordering between them, or from several threads) race and give
+ * undefined results; order them on one stream. */
+int indexer_launch_static(const fp8idx_problem_t *p,
+                          const void *q_bf16, const float *w,
+                          const uint8_t *k_e4m3, const float *k_scale,
+                          const int32_t *page_table, const int32_t *row_pt,
+                          const int32_t *row_bound,
+                          float *scores, int32_t *out_idx, void *stream);
 
 /* Checks the device arrays the calls above trust and writes a status word to
  * `status` (one device uint32, 4-byte aligned; zeroed by this call first, then

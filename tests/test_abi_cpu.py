@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_abi_version_and_strerror(lib):
     import fp8_key_scoring_amd as fk
     assert fk.abi_version() == 1
-    for code in (0, -1, -2, -3, -4, 7):
+    for code in (0, -1, -2, -3, -4, -5, 7):
         assert lib.fp8idx_strerror(code)
 
 
@@ -125,6 +125,21 @@ def test_launch_stage_argument_errors(lib):
     # without caller scores the workspace must also hold them
     ws_own = fk.workspace_size(p, True)
     assert lib.indexer_launch_select(ctypes.byref(p), None, 0x7000, 0xA000, 0x100000, ws_own - 4, None) == -2
+
+
+def test_static_launch_host_errors(lib):
+    """indexer_launch_static rejects a problem over its scratch's limits (more
+    than 256 rows, or a layout over 64 MiB) with -5, and bad arguments with
+    -1, before touching any device."""
+    import fp8_key_scoring_amd as fk
+    good = [0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000]
+    p = fk.make_problem(rows=fk.STATIC_MAX_ROWS + 1, num_pages=16, pt_rows=1, pt_stride=16, max_bound=1024)
+    assert lib.indexer_launch_static(ctypes.byref(p), *good, None, 0x9000, None) == -5
+    # 8 rows x 2M keys with the scores in the scratch: 64 MiB of scores alone
+    p = fk.make_problem(rows=8, num_pages=32768, pt_rows=1, pt_stride=32768, max_bound=1 << 21)
+    assert lib.indexer_launch_static(ctypes.byref(p), *good, None, 0x9000, None) == -5
+    p = fk.make_problem(rows=0, num_pages=16, pt_rows=1, pt_stride=16, max_bound=1024)
+    assert lib.indexer_launch_static(ctypes.byref(p), *good, None, 0x9000, None) == -1
 
 def test_sharded_selection_argument_errors(lib):
     """Host-side checks of the key-sharded calls (nothing is launched: every
