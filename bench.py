@@ -36,9 +36,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--pools", type=int, default=4, help="key-pool copies rotated over")
-    ap.add_argument("--config", type=int, default=3, help="workload 1..7 (3 = 512K keys x 4 rows)")
+    ap.add_argument("--config", type=int, default=3, help="workload 1..8 (3 = 512K keys x 4 rows)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip measuring the device's HBM and MFMA peaks (profiled runs)")
     ap.add_argument("--shards", type=int, default=0,
                     help="time the key-sharded selection instead: one shard's launch, its "
                          "candidates and the merge of G shards (G GPUs emulated on one)")
@@ -535,10 +537,11 @@ def main():
                  "hbm_gbs_at_kernel_time": round(ach_gbs, 1),
                  "mfma_busy_frac": prof.get("mfma_busy_frac"),
                  "score_only_kernel_us": round(score_only_us, 2)})
-    peaks = measured_peaks(torch, dev)
-    mpeak = peaks["bf16_mfma_TFLOPs"] if mfma_bound else peaks["hbm_read_GBs"]
-    roof.update({"measured_peak": mpeak, "frac_of_measured_peak": round(roof["achieved"] / mpeak, 4),
-                 "measured_peaks": peaks})
+    if not args.no_peaks:
+        peaks = measured_peaks(torch, dev)
+        mpeak = peaks["bf16_mfma_TFLOPs"] if mfma_bound else peaks["hbm_read_GBs"]
+        roof.update({"measured_peak": mpeak, "frac_of_measured_peak": round(roof["achieved"] / mpeak, 4),
+                     "measured_peaks": peaks})
     step_roof_s = max(flops / (PEAK_BF16_TFLOPS * 1e12), abytes / (PEAK_HBM_GBS * 1e9))
 
     res = {

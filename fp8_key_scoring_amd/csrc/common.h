@@ -8,6 +8,8 @@
 
 namespace fp8idx {
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 constexpr int kHeads = 64;
 constexpr int kDim = 128;
 constexpr int kPage = 64;
@@ -30,7 +32,7 @@ constexpr int kSliceCap = kMaxTopk + kCandSlice;    // entries (sure keys + cand
 constexpr int kCandCap = 4096;                      // candidates one row may have (else fallback)
 constexpr int kEntCap = kMaxTopk + kCandCap;        // entries of one row finalize holds
 constexpr int kTieCap = 1024;                       // keys in the third-digit bin finalize ranks
-constexpr int kZeroRows = 1024;    // rows the zero block is laid out for (at least)
+constexpr int kZeroRows = 256;     // rows the zero block is laid out for (at least)
 constexpr int kDigit1Bits = 6;      // first radix digit (counted while scoring)
 constexpr int kDigit2Bits = 8;      // second radix digit
 constexpr int kDigit1Shift = 32 - kDigit1Bits;               // 26

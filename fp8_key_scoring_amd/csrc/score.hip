@@ -44,7 +44,6 @@ typedef __bf16 bf16_t;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // 16-key groups loaded ahead per wave (a multiple of 4).  A group feeds 16
 // MFMAs per row, so with 3-4 rows four groups ahead cover as much time as

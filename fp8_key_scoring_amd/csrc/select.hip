@@ -356,72 +356,147 @@ __global__ __launch_bounds__(kSelThreads) void gather_kernel(SelectArgs a) {
 }
 
 // ------------------------------------------------------------- fallback
-// Exact resolution inside the 14-bit prefix bin by one workgroup rescanning
-// the row, used when the candidates overflow their slices: three more digit
-// passes fix the threshold key T (the k-th largest); a last pass in index
-// order then writes the keys above T and the first `need - above` ties at T
-// to the row's output, compacted stably (ascending index).
+// Exact resolution inside the 14-bit prefix bin T14 by one workgroup, used
+// when the row's entries overflow the slices or finalize's LDS (heavy ties,
+// or a very crowded bin).  h3 (LDS) holds gather's third-digit counts of every
+// key in the bin (counted in full, whatever overflowed), so the third digit
+// needs no pass: it gives the 22-bit prefix of the k-th largest key T and the
+// keys still to take inside it.  One pass over the row counts the last 10
+// bits of the keys with that prefix (each thread adds a run of equal digits
+// at once: equal keys are the case here, and adds to one LDS word
+// serialize), which fixes T.  A last pass in index order writes the keys above T and the first
+// ties at T (ascending index), each thread taking 32 consecutive keys, and
+// stops once the row's output is complete.  Both passes keep eight 16-byte
+// loads per thread in flight (32K keys per workgroup step).
 __device__ void fallback_write(const float *row, int b, uint32_t T14, uint32_t need, int32_t *out_row, int k,
-                               uint32_t *h, int *sB, uint32_t *sAbove, uint32_t *wsel, uint32_t *wtie) {
+                               const uint32_t *h3, uint32_t *h10, int *sB, uint32_t *sAbove, uint32_t *wsum) {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int shifts[3] = {10, 2, 0};
-    const int widths[3] = {8, 8, 2};
-    uint32_t prefix = T14;
-    int pshift = kDigit2Shift;
-    uint32_t need_cur = need;
-    for (int d = 0; d < 3; ++d) {
-        if (t < kBins2) h[t] = 0;
-        if (t == 0) { *sB = 0; *sAbove = 0; }
-        __syncthreads();
-        const uint32_t mask = (1u << widths[d]) - 1u;
-        const int sh = shifts[d];
-        for (int64_t base = 0; base < b; base += kSelTile) {
-            uint32_t u[kSelUnroll];
-            load_keys(row, base, b, u);
+    constexpr int kLow = 10;                        // bits below the 22-bit prefix
+    constexpr uint32_t kNone = 0xFFFFFFFFu;
+    for (int i = t; i < (1 << kLow); i += kSelThreads) h10[i] = 0;
+    if (t == 0) { *sB = 0; *sAbove = 0; }
+    __syncthreads();
+    if (t < 64) wave_find_bin(h3, kBins3 / 64, need, lane, sB, sAbove);
+    __syncthreads();
+    const uint32_t T22 = (T14 << kDigit3Bits) | (uint32_t)(*sB);
+    const uint32_t need2 = need - *sAbove;
+    __syncthreads();
+    if (t == 0) { *sB = 0; *sAbove = 0; }
+    // the last 10 bits of the keys with prefix T22: each step 8 x 16-byte
+    // loads per thread (32K keys), all issued before any is used
+    constexpr int kFbVec = 8;
+    constexpr int64_t kFbStep = (int64_t)kFbVec * 4 * kSelThreads;
+    // A step's keys into registers, every load issued before any is used:
+    // 16-byte loads when the whole step lies below the bound and the row is
+    // 16-byte aligned (a caller's score rows need only be 4-byte aligned),
+    // else 4-byte loads at clamped positions (callers test the position).
+    // idx(j) is the first of the four keys of load j.
+    const bool al16 = ((uintptr_t)row & 15) == 0;
+    auto step_keys = [&](int64_t base, auto idx, uint32_t (&u)[kFbVec][4]) {
+        if (al16 && base + kFbStep <= b) {   // (uniform)
 #pragma unroll
-            for (int j = 0; j < kSelUnroll; ++j)
-                if (base + j * kSelThreads + t < b && (u[j] >> pshift) == prefix)
-                    atomicAdd(&h[(u[j] >> sh) & mask], 1u);
+            for (int j = 0; j < kFbVec; ++j) {
+                const u32x4_t v = *(const u32x4_t *)(row + idx(j));
+                u[j][0] = v[0]; u[j][1] = v[1]; u[j][2] = v[2]; u[j][3] = v[3];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kFbVec; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t sj = idx(j) + e;
+                    u[j][e] = __float_as_uint(row[sj < b ? sj : b - 1]);
+                }
         }
-        __syncthreads();
-        if (t < 64) wave_find_bin(h, kBins2 / 64, need_cur, lane, sB, sAbove);
-        __syncthreads();
-        need_cur -= *sAbove;
-        prefix = (prefix << widths[d]) | (uint32_t)(*sB);
-        pshift = shifts[d];
-        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kFbVec; ++j)   // raw bits -> radix keys, in place
+#pragma unroll
+            for (int e = 0; e < 4; ++e) u[j][e] = radix_key(__uint_as_float(u[j][e]));
+    };
+    uint32_t u[kFbVec][4];
+    for (int64_t base = 0; base < b; base += kFbStep) {
+        step_keys(base, [&](int j) { return base + ((int64_t)j * kSelThreads + t) * 4; }, u);
+        // runs of equal digits within a thread's keys are added at once (ties
+        // are the case here, and adds to one LDS word serialize)
+        uint32_t run_d = kNone, run_n = 0;
+#pragma unroll
+        for (int j = 0; j < kFbVec; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t s = base + ((int64_t)j * kSelThreads + t) * 4 + e;
+                const uint32_t uk = u[j][e];
+                if (s < b && (uk >> kLow) == T22) {
+                    const uint32_t d = uk & ((1u << kLow) - 1);
+                    if (d != run_d) {
+                        if (run_n) atomicAdd(&h10[run_d], run_n);
+                        run_d = d;
+                        run_n = 0;
+                    }
+                    ++run_n;
+                }
+            }
+        if (run_n) atomicAdd(&h10[run_d], run_n);
     }
-    const uint32_t T = prefix;   // the k-th largest key; need_cur ties at T to take
+    __syncthreads();
+    if (t < 64) wave_find_bin(h10, (1 << kLow) / 64, need2, lane, sB, sAbove);
+    __syncthreads();
+    const uint32_t T = (T22 << kLow) | (uint32_t)(*sB);   // the k-th largest key
+    const uint32_t need3 = need2 - *sAbove;              // ties at T to take (lowest indices)
+    // output pass: thread t takes the 32 consecutive keys base + 32t ..
+    // base + 32t + 31 (eight 16-byte loads)
     uint32_t sel_run = 0, tie_run = 0;
-    for (int base = 0; base < b; base += kSelThreads) {
-        const int s = base + t;
-        const uint32_t u = s < b ? radix_key(row[s]) : 0u;
-        const bool gt = s < b && u > T;
-        const bool tie = s < b && u == T;
-        const uint64_t mt = __ballot(tie);
-        if (lane == 0) wtie[wave] = (uint32_t)__popcll(mt);
+    for (int64_t base = 0; base < b && sel_run < (uint32_t)k; base += kFbStep) {
+        const int64_t s0 = base + (int64_t)kFbVec * 4 * t;
+        step_keys(base, [&](int j) { return s0 + 4 * j; }, u);
+        uint32_t ngt = 0, ntie = 0;
+#pragma unroll
+        for (int j = 0; j < kFbVec; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool ok = s0 + 4 * j + e < b;
+                ngt += ok && u[j][e] > T;
+                ntie += ok && u[j][e] == T;
+            }
+        // exclusive prefixes over the workgroup of the tie and the
+        // greater-than counts (both <= 32 per thread: ballots on 6 bits)
+        uint32_t tpre = 0, gpre = 0, ttot = 0, gtot = 0;
+#pragma unroll
+        for (int bit = 0; bit < 6; ++bit) {
+            const uint64_t mt = __ballot((ntie >> bit) & 1u), mg = __ballot((ngt >> bit) & 1u);
+            tpre += lane_prefix(mt) << bit;
+            gpre += lane_prefix(mg) << bit;
+            ttot += (uint32_t)__popcll(mt) << bit;
+            gtot += (uint32_t)__popcll(mg) << bit;
+        }
+        if (lane == 0) { wsum[wave] = ttot; wsum[kWaves + wave] = gtot; }
         __syncthreads();
-        uint32_t toff = 0, tall = 0;
-        for (int wv = 0; wv < kWaves; ++wv) {
-            if (wv < wave) toff += wtie[wv];
-            tall += wtie[wv];
+        uint32_t toff = 0, goff = 0, tall = 0, gall = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            if (w < wave) { toff += wsum[w]; goff += wsum[kWaves + w]; }
+            tall += wsum[w];
+            gall += wsum[kWaves + w];
         }
-        const bool sel = gt || (tie && tie_run + toff + lane_prefix(mt) < need_cur);
-        const uint64_t ms = __ballot(sel);
-        if (lane == 0) wsel[wave] = (uint32_t)__popcll(ms);
-        __syncthreads();
-        uint32_t soff = 0, sall = 0;
-        for (int wv = 0; wv < kWaves; ++wv) {
-            if (wv < wave) soff += wsel[wv];
-            sall += wsel[wv];
-        }
-        if (sel) {
-            const uint32_t pos = sel_run + soff + lane_prefix(ms);
-            if (pos < (uint32_t)k) out_row[pos] = s;
-        }
-        sel_run += sall;
+        __syncthreads();   // wsum is written again in the next step
+        uint32_t tr = tie_run + toff + tpre;   // ties before this thread's keys
+        uint32_t pos_g = goff + gpre;           // greater keys before them in this step
+        for (int j = 0; j < kFbVec; ++j)
+            for (int e = 0; e < 4; ++e) {
+                const int64_t s = s0 + 4 * j + e;
+                if (s >= b) break;
+                const uint32_t uk = u[j][e];
+                bool sel = uk > T;
+                if (uk == T) { sel = tr < need3; ++tr; }
+                if (sel) {
+                    // selected keys before this one: earlier steps' (sel_run),
+                    // this step's greater keys and taken ties before it
+                    const uint32_t taken_ties_before = min(tr - (uk == T ? 1u : 0u), need3) - min(tie_run, need3);
+                    const uint32_t pos = sel_run + pos_g + taken_ties_before;
+                    if (pos < (uint32_t)k) out_row[pos] = (int32_t)s;
+                }
+                if (uk > T) ++pos_g;
+            }
+        sel_run += gall + min(tie_run + tall, need3) - min(tie_run, need3);
         tie_run += tall;
-        __syncthreads();
     }
 }
 
@@ -438,7 +513,7 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
     __shared__ uint32_t offe[kSelMaxWgs + 1];
     __shared__ uint32_t roff[kSelMaxWgs + 1];    // exclusive prefix of the entries past 16*kPre per slice
     __shared__ uint32_t h3[kBins3];
-    __shared__ uint32_t wsum[kWaves], wtie[kWaves];
+    __shared__ uint32_t wsum[kWaves], wsum2[2 * kWaves];
     __shared__ int sB;
     __shared__ uint32_t sAbove, ntie, ovf;
     constexpr int kPer = kEntCap / kSelThreads;   // entries per thread
@@ -594,8 +669,8 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
                     ++pos;
                 }
         } else {
-            fallback_write(a.scores + (int64_t)r * a.sstride, b, T14, (uint32_t)need, out_row, k, h3, &sB,
-                           &sAbove, wsum, wtie);
+            fallback_write(a.scores + (int64_t)r * a.sstride, b, T14, (uint32_t)need, out_row, k, h3,
+                           (uint32_t *)ent, &sB, &sAbove, wsum2);
         }
     }
     if (t < kHist1Slots * kBins1) ((uint32_t *)(a.ws + a.L.hist1))[(int64_t)r * kHist1Slots * kBins1 + t] = 0;

@@ -36,7 +36,7 @@
  * be zero-filled once before first use (fp8idx_workspace_init does that on the
  * stream); every launch leaves it zero-filled again, so it can be reused by
  * later launches on the same stream, also for other problem shapes as long as
- * rows <= 1024 (above that, re-initialise it when the row count grows).
+ * rows <= 256 (above that, re-initialise it when the row count grows).
  * Concurrent launches must not share one workspace.
  *
  * Device arrays are trusted for sizes: row_bound[r] must be <= max_bound and
@@ -115,7 +115,10 @@ int fp8idx_workspace_size(const fp8idx_problem_t *p, int scores_in_workspace, si
  * kernel on `stream`. */
 int fp8idx_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
-/* Scoring only: scores[r][s] for every s < row_bound[r] (the causal mask at
+/* Scoring only (the same page, Motivation: every cached key is scored;
+ * Modifications rows 1-2: FP8 -> bf16 conversion, the head reduction, the
+ * per-key scale loaded with each 16-key group, the mask at the store):
+ * scores[r][s] for every s < row_bound[r] (the causal mask at
  * the store); entries at or past the bound are left untouched.  Rows that
  * share a page-table row and sit next to each other in the launch are scored
  * together (each key is read from HBM once for the group).
@@ -127,7 +130,9 @@ int indexer_score(const fp8idx_problem_t *p,
                   const int32_t *row_bound,
                   float *scores, void *stream);
 
-/* Selection only: for each row, the exact top-topk of scores[r][0..bound)
+/* Selection only (the same page, Motivation: the exact top-2048 per row;
+ * Modifications row 4: a radix select whose first digit is radix_key >> 26):
+ * for each row, the exact top-topk of scores[r][0..bound)
  * (descending value; equal values go to the lower key index; NaN ranks below
  * every number; -0 equals +0).  out_idx[r] receives the selected logical
  * indices in ascending index order; with fewer than topk keys all of them
@@ -137,8 +142,9 @@ int indexer_topk(const fp8idx_problem_t *p,
                  const float *scores, const int32_t *row_bound,
                  int32_t *out_idx, void *ws, size_t ws_bytes, void *stream);
 
-/* The fused launch: scoring (with the selection's first radix digit counted
- * in the scoring pass) followed by selection.  `scores` may be NULL (then the
+/* The fused launch (the same page, Motivation and Modifications rows 1-4:
+ * scoring with the selection's first radix digit counted in the scoring
+ * pass, then the exact top-k): scoring followed by selection.  `scores` may be NULL (then the
  * scores live in the workspace); when given, it receives exactly what
  * indexer_score writes.  out_idx as for indexer_topk. */
 int indexer_launch(const fp8idx_problem_t *p,

@@ -239,7 +239,10 @@ CONFIG_NAMES = ["c1_1row_8k", "c2_4rows_128k", "c3_4rows_512k", "c4_8rows_512k_3
                 "c5_256rows_loguniform",
                 # small-row groups over a long context (HBM-bound): one row, and
                 # two verify rows, of one 524,288-key request
-                "c6_1row_512k", "c7_2rows_512k"]
+                "c6_1row_512k", "c7_2rows_512k",
+                # heavy ties at full length: four verify rows over 524,288
+                # copies of one key (every score of a row equal)
+                "c8_4rows_512k_all_equal"]
 
 
 def c5_lengths(rng: np.random.Generator, nreq: int = 64,
@@ -249,7 +252,7 @@ def c5_lengths(rng: np.random.Generator, nreq: int = 64,
 
 
 def make_config(idx: int) -> Problem:
-    """Workload idx in 1..7 (seed 1000 + idx)."""
+    """Workload idx in 1..8 (seed 1000 + idx)."""
     seed = 1000 + idx
     if idx == 1:
         return build_problem(CONFIG_NAMES[0], seed, [8192], [(0, 8192)])
@@ -276,6 +279,9 @@ def make_config(idx: int) -> Problem:
     if idx == 7:
         n = 524288
         return build_problem(CONFIG_NAMES[6], seed, [n], verify_rows(0, n, 2))
+    if idx == 8:
+        n = 524288
+        return build_problem(CONFIG_NAMES[7], seed, [n], verify_rows(0, n), key_mode="all_equal")
     raise ValueError(idx)
 
 

@@ -160,7 +160,7 @@ def _zero_block_bytes(rows):
     part every launch must find zero and leaves zero; the rest is scratch a
     launch writes before it reads (sizes as the library lays them out)."""
     al = lambda x: (x + 255) // 256 * 256
-    rz = max(rows, 1024)
+    rz = max(rows, 256)
     return al(rz * 16 * 64 * 4) + al(rz * 8 * 256 * 4) + al(rz * 256 * 4)
 
 

@@ -89,6 +89,39 @@ def test_all_equal_keys_take_the_lowest_indices():
         assert out[r].tolist() == list(range(2048))
 
 
+def test_heavy_tie_fallback_rows_through_topk():
+    # rows whose prefix bin at the threshold holds far more keys than the
+    # selection keeps in LDS, so the exact fallback decides them: (a) one
+    # value everywhere plus 1,500 larger keys scattered; (b) three adjacent
+    # floats over 150,000 keys with 900 larger ones (several distinct last
+    # digits); (c) the same as (a) in a score buffer whose rows are not
+    # 16-byte aligned (offset by one float, odd stride)
+    import torch
+    import fp8_key_scoring_amd as fk
+    import oracle
+    rng = np.random.default_rng(17)
+    n = 200000
+    a = np.ones(n, np.float32)
+    a[rng.choice(n, 1500, replace=False)] = 2.0
+    b = np.array([1.0, np.nextafter(np.float32(1.0), np.float32(2.0)),
+                  np.nextafter(np.nextafter(np.float32(1.0), np.float32(2.0)), np.float32(2.0))], np.float32)
+    bb = b[rng.integers(0, 3, size=n)].astype(np.float32)
+    bb[150000:] = np.nan                      # past the row's bound (never read)
+    bb[rng.choice(150000, 900, replace=False)] = 3.0
+    rows = np.stack([a, bb, a])
+    bounds = np.array([n, 150000, n], np.int32)
+    say("[gpu] heavy-tie fallback through indexer_topk (aligned and unaligned rows)")
+    for offset in (0, 1):
+        buf = torch.full((3, n + 1 + offset), float("nan"), dtype=torch.float32, device="cuda:0")
+        sc = buf[:, offset:offset + n] if offset == 0 else buf[:, offset:offset + n + 1]
+        sc[:, :n] = torch.from_numpy(rows).to("cuda:0")
+        rb = torch.from_numpy(bounds).to("cuda:0")
+        out = fk.indexer_topk(sc, rb, max_bound=n).cpu().numpy()
+        for r in range(3):
+            want = np.sort(oracle.topk(np.ascontiguousarray(rows[r, :bounds[r]]), 2048))
+            assert np.array_equal(out[r], want), (offset, r)
+
+
 def test_ties_straddling_the_threshold():
     p = syn.scale_tie_problem(n=12000)
     scores, out = full_check(p, "scale_ties")
@@ -158,6 +191,16 @@ def test_c7_two_rows_512k():
     _big(7)
 
 
+def test_c8_all_equal_keys_512k():
+    # every score of each 524,288-key row equal: the exact answer is keys
+    # 0..2047, reached through the heavy-tie fallback at full length
+    _big(8, overlap_rows=[0, 3])
+    p = syn.make_config(8)
+    scores, out = run_launch(p)
+    for r in range(p.rows):
+        assert out[r].tolist() == list(range(2048))
+
+
 def test_one_row_1200k_multi_step_slices():
     # a row longer than 64 x 8,192 keys: each selection workgroup scans
     # several 8K-key steps of its slice (refine's and gather's step loop
@@ -177,7 +220,7 @@ def test_one_row_1200k_multi_step_slices():
 
 
 def test_1100_rows_more_than_the_zero_block_layout():
-    # more rows than the 1,024 the workspace's zero block is laid out for by
+    # more rows than the 256 the workspace's zero block is laid out for by
     # default: the block is then sized by the row count
     lens = [300 + (i * 37) % 2900 for i in range(275)]
     rows = []
