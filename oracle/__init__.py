@@ -58,6 +58,8 @@ def _load():
         lib.oracle_topk_f32.argtypes = [P, I64, I, P]
         lib.oracle_topk_f64.restype = I
         lib.oracle_topk_f64.argtypes = [P, I64, I, P]
+        lib.oracle_sparse_attention.restype = I
+        lib.oracle_sparse_attention.argtypes = [P, P, I, P, I, I, I, P, I, I, ctypes.c_double, P, P]
         _lib = lib
     return _lib
 
@@ -199,3 +201,37 @@ def write_new_keys(p, k_new_bf16: np.ndarray):
         k8[page, (b - 1) % 64, :] = codes
         ks[page, (b - 1) % 64] = sc
     return k8, ks
+
+
+ATTN_HEADS = 16
+ATTN_DIM = 576
+ATTN_VDIM = 512
+
+
+def sparse_attention(q_bf16: np.ndarray, kv_bf16: np.ndarray, page_table: np.ndarray, row_pt: np.ndarray,
+                     sel: np.ndarray, max_bound: int, sm_scale: float, rows=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Sparse attention of each row's 16 heads over its selected key
+    positions (oracle.c states the reading): returns (out [rows, 16, 512]
+    fp64, lse [rows, 16] fp64) for the given rows (all by default).
+
+    q_bf16 [R, 16, 576] and kv_bf16 [pages, 64, 576] are raw bf16 patterns
+    (uint16); sel [R, topk] int32 logical positions, -1 for none."""
+    q = np.ascontiguousarray(q_bf16, dtype=np.uint16)
+    kv = np.ascontiguousarray(kv_bf16, dtype=np.uint16)
+    pt = np.ascontiguousarray(page_table, dtype=np.int32)
+    sl = np.ascontiguousarray(sel, dtype=np.int32)
+    rows = range(q.shape[0]) if rows is None else rows
+    rows = list(rows)
+    out = np.zeros((len(rows), ATTN_HEADS, ATTN_VDIM), np.float64)
+    lse = np.zeros((len(rows), ATTN_HEADS), np.float64)
+    for i, r in enumerate(rows):
+        o = np.zeros((ATTN_HEADS, ATTN_VDIM), np.float64)
+        l = np.zeros(ATTN_HEADS, np.float64)
+        rc = _load().oracle_sparse_attention(_p(q[r]), _p(kv), int(kv.shape[0]), _p(pt), int(pt.shape[0]),
+                                             int(pt.shape[1]), int(row_pt[r]), _p(sl[r]), int(sl.shape[1]),
+                                             int(max_bound), float(sm_scale), _p(o), _p(l))
+        if rc != 0:
+            raise RuntimeError(f"oracle_sparse_attention failed: {rc}")
+        out[i] = o
+        lse[i] = l
+    return out, lse

@@ -316,3 +316,95 @@ int oracle_quantize_key(const uint16_t *k_bf16, uint8_t *codes, float *scale_out
 }
 
 uint8_t oracle_e4m3_nearest(float x) { return e4m3_nearest(x); }
+
+/*
+ * Sparse attention over a row's selected keys: the step the indexer feeds
+ * (the sglang pull request page, #86 commit body, Motivation: the launch
+ * picks each row's exact top-2048 keys for the attention that follows; the
+ * GLM-5.2 release test-suite page runs that step with an MLA sparse
+ * attention backend over a DeepSeek-style latent cache).  The pages give
+ * neither the formula nor the shapes; the reading used here is multi-head
+ * latent attention in its absorbed decode form:
+ *
+ *   every key position s of a request holds one latent vector c_s of 576
+ *   bf16 values (512 latent + 64 rotary), paged like the index keys (the
+ *   same page table: page page_table[row_pt][s / 64], slot s % 64);
+ *   row r has 16 query heads q_h of 576 bf16 values;
+ *   for the row's selected positions J (its index list, -1 entries skipped;
+ *   a position outside [0, max_bound) or on a page id out of range is
+ *   skipped too):
+ *     l_j   = sm_scale * sum_{i<576} q_h[i] * c_j[i]
+ *     out_h = sum_j exp(l_j) * c_j[0..512) / sum_j exp(l_j)
+ *     lse_h = log(sum_j exp(l_j))
+ *   with no selected position: out_h = 0, lse_h = -inf.
+ *
+ * fp64 throughout; exp and log of fp64, the sums in index-list order, the
+ * maximum logit subtracted before exp (exp(l - m) / sum exp(l - m) is the
+ * same quotient).
+ */
+#define ORC_AH 16
+#define ORC_AD 576
+#define ORC_AV 512
+
+int oracle_sparse_attention(const uint16_t *q_r, const uint16_t *kv, int num_pages,
+                            const int32_t *page_table, int pt_rows, int pt_stride, int row_pt,
+                            const int32_t *sel_r, int topk, int max_bound, double sm_scale,
+                            double *out_r, double *lse_r)
+{
+    if (!q_r || !kv || !page_table || !sel_r || !out_r || !lse_r || topk < 0 || num_pages < 1)
+        return -1;
+    /* the selected positions' cache rows (NULL: skipped) */
+    const uint16_t **rowp = (const uint16_t **)malloc(sizeof(const uint16_t *) * (size_t)(topk > 0 ? topk : 1));
+    double *lg = (double *)malloc(sizeof(double) * (size_t)(topk > 0 ? topk : 1));
+    if (!rowp || !lg) {
+        free(rowp);
+        free(lg);
+        return -1;
+    }
+    for (int j = 0; j < topk; ++j) {
+        const int32_t s = sel_r[j];
+        rowp[j] = NULL;
+        if (s < 0 || s >= max_bound || row_pt < 0 || row_pt >= pt_rows || s / ORC_PAGE >= pt_stride)
+            continue;
+        const int32_t pg = page_table[(int64_t)row_pt * pt_stride + s / ORC_PAGE];
+        if (pg < 0 || pg >= num_pages)
+            continue;
+        rowp[j] = kv + ((int64_t)pg * ORC_PAGE + s % ORC_PAGE) * ORC_AD;
+    }
+    for (int h = 0; h < ORC_AH; ++h) {
+        const uint16_t *q = q_r + (int64_t)h * ORC_AD;
+        double m = -INFINITY;
+        for (int j = 0; j < topk; ++j) {
+            if (!rowp[j])
+                continue;
+            double d = 0.0;
+            for (int i = 0; i < ORC_AD; ++i)
+                d += bf16_value(q[i]) * bf16_value(rowp[j][i]);
+            lg[j] = sm_scale * d;
+            if (lg[j] > m)
+                m = lg[j];
+        }
+        double *o = out_r + (int64_t)h * ORC_AV;
+        for (int i = 0; i < ORC_AV; ++i)
+            o[i] = 0.0;
+        if (m == -INFINITY) {   /* nothing selected */
+            lse_r[h] = -INFINITY;
+            continue;
+        }
+        double den = 0.0;
+        for (int j = 0; j < topk; ++j) {
+            if (!rowp[j])
+                continue;
+            const double p = exp(lg[j] - m);
+            den += p;
+            for (int i = 0; i < ORC_AV; ++i)
+                o[i] += p * bf16_value(rowp[j][i]);
+        }
+        for (int i = 0; i < ORC_AV; ++i)
+            o[i] /= den;
+        lse_r[h] = m + log(den);
+    }
+    free(rowp);
+    free(lg);
+    return 0;
+}
