@@ -23,6 +23,7 @@ MAX_TOPK = 2048
 EXPORTED = ("fp8idx_abi_version", "fp8idx_strerror", "fp8idx_workspace_size",
             "fp8idx_workspace_init", "indexer_score", "indexer_topk", "indexer_launch",
             "indexer_launch_score", "indexer_launch_select", "indexer_launch_static",
+            "fp8idx_attention_workspace_size", "indexer_sparse_attention",
             "indexer_shard_candidates", "indexer_merge_topk", "indexer_write_keys",
             "indexer_launch_new_keys", "indexer_validate")
 
@@ -80,6 +81,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.indexer_launch_select.argtypes = [ctypes.POINTER(Problem), P, P, P, P, ctypes.c_size_t, P]
     lib.indexer_launch_static.restype = ctypes.c_int
     lib.indexer_launch_static.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, P, P, P, P, P]
+    lib.fp8idx_attention_workspace_size.restype = ctypes.c_int
+    lib.fp8idx_attention_workspace_size.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(ctypes.c_size_t)]
+    lib.indexer_sparse_attention.restype = ctypes.c_int
+    lib.indexer_sparse_attention.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P, ctypes.c_float, P, P, P,
+                                             ctypes.c_size_t, P]
     lib.indexer_validate.restype = ctypes.c_int
     lib.indexer_validate.argtypes = [ctypes.POINTER(Problem), P, P, P, P, P]
     lib.indexer_write_keys.restype = ctypes.c_int
@@ -418,3 +424,49 @@ def indexer_merge_topk(cand_score, cand_idx, *, shards: int, topk: int = MAX_TOP
     _check(load_library().indexer_merge_topk(ctypes.byref(prob), shards, _ptr(cand_score), _ptr(cand_idx),
                                              _ptr(out_idx), _stream(cand_idx.device)))
     return out_idx
+
+
+ATTN_HEADS = 16
+ATTN_DIM = 576
+ATTN_VDIM = 512
+
+
+def attention_workspace(rows: int, topk: int, device):
+    """Workspace tensor (uint8, 256-byte aligned) for indexer_sparse_attention."""
+    import torch
+    prob = make_problem(rows=rows, num_pages=1, pt_rows=1, pt_stride=1, max_bound=0, topk=topk)
+    n = ctypes.c_size_t(0)
+    _check(load_library().fp8idx_attention_workspace_size(ctypes.byref(prob), ctypes.byref(n)))
+    ws = torch.empty(int(n.value) + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + int(n.value)]
+
+
+def indexer_sparse_attention(q_attn, kv, page_table, row_pt, sel, *, max_bound: int, sm_scale: float,
+                             out=None, lse=None, workspace=None):
+    """Attention of each row's 16 heads (q_attn [rows, 16, 576] bf16) over its
+    selected positions sel [rows, topk] int32 (-1: none) in the paged latent
+    cache kv [pages, 64, 576] bf16 (same page table as the index keys).
+    Returns (out [rows, 16, 512] fp32, lse [rows, 16] fp32)."""
+    import torch
+    R = q_attn.shape[0]
+    assert q_attn.dtype == torch.bfloat16 and tuple(q_attn.shape[1:]) == (ATTN_HEADS, ATTN_DIM) and q_attn.is_contiguous()
+    assert kv.dtype == torch.bfloat16 and tuple(kv.shape[1:]) == (PAGE, ATTN_DIM) and kv.is_contiguous()
+    assert page_table.dtype == torch.int32 and page_table.dim() == 2 and page_table.is_contiguous()
+    assert row_pt.dtype == torch.int32 and tuple(row_pt.shape) == (R,) and row_pt.is_contiguous()
+    assert sel.dtype == torch.int32 and sel.dim() == 2 and sel.shape[0] == R and sel.is_contiguous()
+    topk = sel.shape[1]
+    if out is None:
+        out = torch.empty((R, ATTN_HEADS, ATTN_VDIM), dtype=torch.float32, device=q_attn.device)
+    if lse is None:
+        lse = torch.empty((R, ATTN_HEADS), dtype=torch.float32, device=q_attn.device)
+    assert out.dtype == torch.float32 and tuple(out.shape) == (R, ATTN_HEADS, ATTN_VDIM) and out.is_contiguous()
+    assert lse.dtype == torch.float32 and tuple(lse.shape) == (R, ATTN_HEADS) and lse.is_contiguous()
+    if workspace is None:
+        workspace = attention_workspace(R, topk, q_attn.device)
+    prob = make_problem(rows=R, num_pages=kv.shape[0], pt_rows=page_table.shape[0], pt_stride=page_table.shape[1],
+                        max_bound=max_bound, topk=topk)
+    _check(load_library().indexer_sparse_attention(ctypes.byref(prob), _ptr(q_attn), _ptr(kv), _ptr(page_table),
+                                                   _ptr(row_pt), _ptr(sel), float(sm_scale), _ptr(out), _ptr(lse),
+                                                   _ptr(workspace), workspace.numel(), _stream(q_attn.device)))
+    return out, lse

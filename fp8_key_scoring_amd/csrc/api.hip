@@ -289,6 +289,55 @@ int indexer_launch_static(const fp8idx_problem_t *p, const void *q_bf16, const f
     return rc;
 }
 
+int fp8idx_attention_workspace_size(const fp8idx_problem_t *p, size_t *bytes) {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if (!bytes) return FP8IDX_EINVAL;
+    *bytes = attn_workspace_bytes(p->rows, p->topk);
+    return FP8IDX_OK;
+}
+
+int indexer_sparse_attention(const fp8idx_problem_t *p, const void *q_bf16, const void *kv_bf16,
+                             const int32_t *page_table, const int32_t *row_pt, const int32_t *sel,
+                             float sm_scale, float *out, float *lse, void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if (p->num_pages < 1 || p->pt_rows < 1 || p->pt_stride < 1) return FP8IDX_EINVAL;
+    if ((int64_t)p->max_bound > (int64_t)p->pt_stride * FP8IDX_PAGE) return FP8IDX_EINVAL;
+    if (!q_bf16 || !kv_bf16 || !page_table || !row_pt || !sel || !out || !lse) return FP8IDX_EINVAL;
+    if (!aligned(q_bf16, 16) || !aligned(kv_bf16, 16) || !aligned(page_table, 4) || !aligned(row_pt, 4) ||
+        !aligned(sel, 4) || !aligned(out, 4) || !aligned(lse, 4))
+        return FP8IDX_EINVAL;
+    if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY) return FP8IDX_EINVAL;
+    if ((int64_t)p->num_pages * FP8IDX_PAGE > INT32_MAX) return FP8IDX_EINVAL;   // cache rows as int32
+    const size_t need = attn_workspace_bytes(p->rows, p->topk);
+    if (!ws || !aligned(ws, 256) || ws_bytes < need) return FP8IDX_EWORKSPACE;
+    rc = check_device();
+    if (rc) return rc;
+    AttnArgs a;
+    a.q = (const uint16_t *)q_bf16;
+    a.kv = (const uint16_t *)kv_bf16;
+    a.page_table = page_table;
+    a.row_pt = row_pt;
+    a.sel = sel;
+    a.out = out;
+    a.lse = lse;
+    int n, sp;
+    attn_split(p->rows, p->topk, &n, &sp);
+    a.part_o = (float *)ws;
+    a.part_ml = (float *)((unsigned char *)ws + align_up((size_t)p->rows * n * kAttnHeads * kAttnVDim * 4, 256));
+    a.sm_scale = sm_scale;
+    a.rows = p->rows;
+    a.topk = p->topk;
+    a.span = sp;
+    a.nsplit = n;
+    a.num_pages = p->num_pages;
+    a.pt_rows = p->pt_rows;
+    a.pt_stride = p->pt_stride;
+    a.max_bound = p->max_bound;
+    return to_code(launch_attention(a, (hipStream_t)stream));
+}
+
 int indexer_validate(const fp8idx_problem_t *p, const int32_t *page_table, const int32_t *row_pt,
                      const int32_t *row_bound, uint32_t *status, void *stream) {
     int rc = check_problem(p);

@@ -148,6 +148,50 @@ struct SelectArgs {
     int rows, max_bound, topk;
 };
 
+// ---- sparse attention over the selected keys (attn.hip)
+constexpr int kAttnHeads = 16;    // query heads per row
+constexpr int kAttnDim = 576;     // latent (512) + rotary (64) dims of a cache row and a query head
+constexpr int kAttnVDim = 512;    // value dims (the latent part)
+constexpr int kAttnMaxSplit = 32; // workgroups one row's index list is split over (at most)
+
+struct AttnArgs {
+    const uint16_t *q;        // [rows][16][576] bf16
+    const uint16_t *kv;       // [num_pages][64][576] bf16
+    const int32_t *page_table;
+    const int32_t *row_pt;
+    const int32_t *sel;       // [rows][topk] logical positions, -1 none
+    float *out;               // [rows][16][512]
+    float *lse;               // [rows][16]
+    float *part_o;            // [rows][nsplit][16][512]  (workspace)
+    float *part_ml;           // [rows][nsplit][2][16]    (workspace)
+    float sm_scale;
+    int rows, topk, span, nsplit, num_pages, pt_rows, pt_stride, max_bound;
+};
+
+// A row's index list is split over nsplit workgroups of span entries (a
+// multiple of 64) so that rows * nsplit reaches about 256 workgroups.
+inline void attn_split(int rows, int topk, int *nsplit, int *span) {
+    int n = (256 + rows - 1) / rows;
+    const int chunks = (topk + 63) / 64;
+    if (n > chunks) n = chunks;
+    if (n > kAttnMaxSplit) n = kAttnMaxSplit;
+    if (n < 1) n = 1;
+    int sp = (topk + n - 1) / n;
+    sp = (sp + 63) / 64 * 64;
+    if (sp < 64) sp = 64;
+    *span = sp;
+    *nsplit = (topk + sp - 1) / sp > 0 ? (topk + sp - 1) / sp : 1;
+}
+
+inline size_t attn_workspace_bytes(int rows, int topk) {
+    int n, sp;
+    attn_split(rows, topk, &n, &sp);
+    const size_t o = align_up((size_t)rows * n * kAttnHeads * kAttnVDim * 4, 256);
+    return o + (size_t)rows * n * 2 * kAttnHeads * 4;
+}
+
+hipError_t launch_attention(const AttnArgs &a, hipStream_t st);
+
 hipError_t launch_score(const ScoreArgs &a, hipStream_t st);
 hipError_t launch_hist1(const SelectArgs &a, hipStream_t st);
 hipError_t launch_refine(const SelectArgs &a, hipStream_t st);

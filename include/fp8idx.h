@@ -291,6 +291,46 @@ int indexer_merge_topk(const fp8idx_problem_t *p, int shards,
                        const float *cand_score, const int32_t *cand_idx,
                        int32_t *out_idx, void *stream);
 
+/* ---- Sparse attention over each row's selected keys: the step the indexer
+ * feeds (the same sglang page, Motivation: the exact top-2048 keys of each
+ * row are picked for the attention after it; the release test-suite page for
+ * GLM-5.2 runs that step as MLA sparse attention over a DeepSeek-style latent
+ * cache).  The pages give no formula or shapes; the reading is absorbed
+ * multi-head latent attention at decode:
+ *   kv          [num_pages][64][576]   bf16 latent cache (512 latent + 64
+ *                                      rotary values per key), 16-B aligned,
+ *                                      paged by the same page_table / row_pt
+ *                                      as the index keys
+ *   q_bf16      [rows][16][576]        bf16 absorbed queries, 16-B aligned
+ *   sel         [rows][topk]           int32 logical key positions (the
+ *                                      indexer's out_idx); -1 = none
+ *   out         [rows][16][512]        fp32
+ *   lse         [rows][16]             fp32
+ * For row r and head h, over the selected positions j (an entry is skipped
+ * when it is negative, at or past max_bound, or on a page id outside
+ * [0, num_pages); a repeated position counts each time):
+ *   l_j = sm_scale * q[r][h] . kv(j),   out[r][h] = sum_j e^{l_j} kv(j)[0..512) / sum_j e^{l_j},
+ *   lse[r][h] = log sum_j e^{l_j};  nothing selected: out 0, lse -inf.
+ * Logits are fp32 sums of exact bf16 products; the softmax weights enter the
+ * value sum with about 16 significant bits; sums are fp32.
+ *
+ * Bytes of workspace for indexer_sparse_attention with p->rows and p->topk
+ * (per-split partial outputs); host-only. */
+int fp8idx_attention_workspace_size(const fp8idx_problem_t *p, size_t *bytes);
+
+/* Enqueues the attention on `stream`.  Uses every field of `p` but
+ * score_stride (rows, topk = entries per row of sel; num_pages, pt_rows,
+ * pt_stride, max_bound as for the indexer).  `ws` (256-byte aligned, at least
+ * fp8idx_attention_workspace_size bytes) is scratch: no initialisation is
+ * needed and its contents are overwritten.  Errors: -1 for a null or
+ * misaligned pointer, a non-finite sm_scale or a bad problem; -2 for a
+ * missing or short workspace; row_pt entries outside [0, pt_rows) select
+ * nothing. */
+int indexer_sparse_attention(const fp8idx_problem_t *p, const void *q_bf16, const void *kv_bf16,
+                             const int32_t *page_table, const int32_t *row_pt, const int32_t *sel,
+                             float sm_scale, float *out, float *lse, void *ws, size_t ws_bytes,
+                             void *stream);
+
 #ifdef __cplusplus
 }
 #endif

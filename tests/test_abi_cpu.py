@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
               "fp8idx_workspace_init", "fp8idx_abi_version", "fp8idx_strerror",
               "indexer_shard_candidates", "indexer_merge_topk", "indexer_write_keys",
               "indexer_launch_new_keys", "indexer_validate", "indexer_launch_score",
-              "indexer_launch_select"):
+              "indexer_launch_select", "indexer_launch_static", "fp8idx_attention_workspace_size",
+              "indexer_sparse_attention"):
         assert n in names
 
 
@@ -215,6 +216,44 @@ def test_validate_argument_errors(lib):
     assert v(ok, ptrs) == -1
     bad = fk.make_problem(rows=4, num_pages=16, pt_rows=1, pt_stride=16, max_bound=16 * 64 + 1, topk=2048)
     assert v(bad, P) == -1
+
+
+def test_attention_argument_errors(lib):
+    import fp8_key_scoring_amd as fk
+    ok = fk.make_problem(rows=4, num_pages=16, pt_rows=1, pt_stride=16, max_bound=1024, topk=2048)
+    n = ctypes.c_size_t(0)
+    assert lib.fp8idx_attention_workspace_size(ctypes.byref(ok), ctypes.byref(n)) == 0
+    # 4 rows: 32 splits of 64 keys; partial outputs 4*32*16*512 fp32 + maxima and sums
+    assert n.value == 4 * 32 * 16 * 512 * 4 + 4 * 32 * 2 * 16 * 4
+    assert lib.fp8idx_attention_workspace_size(ctypes.byref(ok), None) == -1
+    one = fk.make_problem(rows=1000, num_pages=16, pt_rows=1, pt_stride=16, max_bound=1024, topk=2048)
+    assert lib.fp8idx_attention_workspace_size(ctypes.byref(one), ctypes.byref(n)) == 0
+    assert n.value == 1000 * 16 * 512 * 4 + 1000 * 2 * 16 * 4 + (-(1000 * 16 * 512 * 4)) % 256
+    big = n.value
+    # q, kv, page_table, row_pt, sel, out, lse: never dereferenced
+    P = [0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000]
+    a = lambda p, ptrs, sm=0.1, ws=0x100000, wsb=1 << 30: lib.indexer_sparse_attention(
+        ctypes.byref(p), *ptrs[:5], ctypes.c_float(sm), *ptrs[5:], ws, wsb, None)
+    for i in range(7):
+        ptrs = list(P)
+        ptrs[i] = None
+        assert a(ok, ptrs) == -1, i
+    for i, al in ((0, 0x1008), (1, 0x2008), (4, 0x5002)):   # q, kv 16-byte; sel 4-byte
+        ptrs = list(P)
+        ptrs[i] = al
+        assert a(ok, ptrs) == -1, i
+    for sm in (float("nan"), float("inf"), float("-inf")):
+        assert a(ok, P, sm=sm) == -1
+    assert a(ok, P, ws=None) == -2
+    assert a(ok, P, ws=0x100080) == -2                      # 256-byte alignment
+    assert a(ok, P, wsb=16) == -2
+    assert a(one, P, wsb=big - 4) == -2
+    bad = fk.make_problem(rows=4, num_pages=16, pt_rows=1, pt_stride=16, max_bound=16 * 64 + 1, topk=2048)
+    assert a(bad, P) == -1
+    for kw in (dict(rows=0), dict(topk=0), dict(topk=2049)):
+        args = dict(rows=4, num_pages=16, pt_rows=1, pt_stride=16, max_bound=1024, topk=2048)
+        args.update(kw)
+        assert a(fk.make_problem(**args), P) == -1, kw
 
 
 def test_header_is_plain_c_and_links(tmp_path):
