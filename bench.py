@@ -14,6 +14,7 @@ and on one core).
 """
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -47,6 +48,9 @@ def parse():
     ap.add_argument("--new-keys", action="store_true",
                     help="time the launch with the new-key write instead: the write alone, the "
                          "launch without and with it")
+    ap.add_argument("--attention", action="store_true",
+                    help="time the sparse attention over the selected keys (the step after the launch) "
+                         "on the workload's rows and page table")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -381,6 +385,73 @@ def new_keys_report(args):
                       "trials": 5, "steps": args.steps}))
 
 
+def attention_report(args):
+    """Sparse attention over each row's selected keys on the workload's rows:
+    16 heads x 576 over a bf16 latent cache paged like the index keys.  Timed
+    over back-to-back calls between HIP events on the call's stream, with the
+    selection rotated over enough seeded random selections (each row's topk
+    distinct positions below its bound, as the indexer's output is) that their
+    cache rows exceed the 256 MB last-level cache; also the indexer's own
+    selection repeated (its rows stay cache-resident: `us_hot`).  The roofline
+    figure is that of the whole call (the attention kernel and, with more than
+    one split per row, the combine); the rocprofv3 trace of the same command
+    splits it by kernel."""
+    import torch
+    import fp8_key_scoring_amd as fk
+    import synthetic as syn
+    fk.load_library()
+    dev = "cuda:0"
+    p = syn.make_config(args.config)
+    d = syn.device_arrays(p, dev)
+    mb, k = p.max_bound, p.topk
+    q_attn, kv = syn.attention_inputs_device(p, 2024, dev)
+    sel_idx = fk.indexer_launch(**d, max_bound=mb, topk=k)
+    row_bytes = syn.ATTN_DIM * 2
+    per_sel = p.rows * k * row_bytes
+    nsel = max(2, int(math.ceil(2 * 256e6 / per_sel)))
+    nsel = min(nsel, 64)
+    sels = syn.random_selections_device(p, 77, nsel, dev)
+    out = torch.empty((p.rows, syn.ATTN_HEADS, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((p.rows, syn.ATTN_HEADS), dtype=torch.float32, device=dev)
+    ws = fk.attention_workspace(p.rows, k, dev)
+    sm = 1.0 / math.sqrt(192.0)
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def call(s):
+        fk.indexer_sparse_attention(q_attn, kv, d["page_table"], d["row_pt"], s, max_bound=mb, sm_scale=sm,
+                                    out=out, lse=lse, workspace=ws)
+
+    def timed(pick, n):
+        for i in range(min(args.warmup, n)):
+            call(pick(i))
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            call(pick(i))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    rot, hot = [], []
+    for _ in range(5):
+        rot.append(timed(lambda i: sels[i % nsel], args.steps))
+        hot.append(timed(lambda i: sel_idx, args.steps))
+    us = float(np.median(rot))
+    valid = int(sum(min(int(b), k) for b in p.row_bound))
+    alg = valid * row_bytes + p.rows * k * 4 + p.rows * syn.ATTN_HEADS * (syn.ATTN_DIM * 2 + 512 * 4 + 4)
+    print(json.dumps({"metric": "sparse attention over the selected keys: µs per call",
+                      "config": {"workload": p.name, "rows": p.rows, "topk": k, "heads": syn.ATTN_HEADS,
+                                 "dim": syn.ATTN_DIM, "selections_rotated": nsel},
+                      "us": round(us, 2), "us_trials": [round(x, 2) for x in rot],
+                      "us_hot": round(float(np.median(hot)), 2),
+                      "algorithmic_bytes": alg,
+                      "call_roofline": {"bound": "hbm", "achieved": round(alg / us / 1e3, 1), "peak": 8000.0,
+                                        "unit": "GB/s", "frac": round(alg / us / 1e3 / 8000.0, 4)},
+                      "steps": args.steps}))
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -395,6 +466,9 @@ def main():
         return
     if args.new_keys:
         new_keys_report(args)
+        return
+    if args.attention:
+        attention_report(args)
         return
     import synthetic as syn
     p = syn.make_config(args.config)

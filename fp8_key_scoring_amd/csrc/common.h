@@ -152,7 +152,8 @@ struct SelectArgs {
 constexpr int kAttnHeads = 16;    // query heads per row
 constexpr int kAttnDim = 576;     // latent (512) + rotary (64) dims of a cache row and a query head
 constexpr int kAttnVDim = 512;    // value dims (the latent part)
-constexpr int kAttnMaxSplit = 32; // workgroups one row's index list is split over (at most)
+constexpr int kAttnMaxSplit = 32;     // workgroups one row's index list is split over (at most)
+constexpr int kAttnWaveChunk = 16;    // index-list entries one wave takes at a time
 
 struct AttnArgs {
     const uint16_t *q;        // [rows][16][576] bf16
@@ -171,14 +172,15 @@ struct AttnArgs {
 // A row's index list is split over nsplit workgroups of span entries (a
 // multiple of 64) so that rows * nsplit reaches about 256 workgroups.
 inline void attn_split(int rows, int topk, int *nsplit, int *span) {
+    // about 256 workgroups in all; a workgroup (4 waves) takes at least one
+    // chunk of kAttnWaveChunk entries per wave
     int n = (256 + rows - 1) / rows;
-    const int chunks = (topk + 63) / 64;
-    if (n > chunks) n = chunks;
+    const int units = (topk + 4 * kAttnWaveChunk - 1) / (4 * kAttnWaveChunk);
+    if (n > units) n = units;
     if (n > kAttnMaxSplit) n = kAttnMaxSplit;
     if (n < 1) n = 1;
     int sp = (topk + n - 1) / n;
-    sp = (sp + 63) / 64 * 64;
-    if (sp < 64) sp = 64;
+    sp = (sp + kAttnWaveChunk - 1) / kAttnWaveChunk * kAttnWaveChunk;
     *span = sp;
     *nsplit = (topk + sp - 1) / sp > 0 ? (topk + sp - 1) / sp : 1;
 }

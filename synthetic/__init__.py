@@ -373,3 +373,45 @@ def new_keys(p: Problem, seed: int = 0, special: bool = True) -> np.ndarray:
         for i, e in enumerate(edge[:p.rows]):
             kf[i] = e
     return bf16_bits_rne(kf)
+
+
+# --------------------------------------------------------------------------
+# inputs of the sparse attention after the indexer
+# --------------------------------------------------------------------------
+ATTN_HEADS = 16     # query heads per row (absorbed MLA decode)
+ATTN_DIM = 576      # latent (512) + rotary (64) values per cache row
+
+
+def attention_inputs_device(p: Problem, seed: int, device):
+    """Seeded inputs of the sparse attention for problem ``p``, drawn on the
+    device with torch's generator (sizes the numpy path would take seconds
+    for): q_attn [rows, 16, 576] and a latent cache [num_pages, 64, 576], both
+    N(0,1) rounded to bf16 by torch's cast.  The cache shares ``p``'s page
+    table."""
+    import torch
+    g = torch.Generator(device=device).manual_seed(seed)
+    q = torch.randn((p.rows, ATTN_HEADS, ATTN_DIM), generator=g, device=device).to(torch.bfloat16)
+    kv = torch.empty((p.num_pages, PAGE, ATTN_DIM), dtype=torch.bfloat16, device=device)
+    step = 1024   # pages per draw, so the fp32 draw stays small
+    for p0 in range(0, p.num_pages, step):
+        p1 = min(p.num_pages, p0 + step)
+        kv[p0:p1] = torch.randn((p1 - p0, PAGE, ATTN_DIM), generator=g, device=device).to(torch.bfloat16)
+    return q, kv
+
+
+def random_selections_device(p: Problem, seed: int, count: int, device):
+    """``count`` seeded selections [rows, topk] int32 for problem ``p``: row r
+    takes topk distinct positions below its bound (all of them, then -1, when
+    the bound is smaller), in random order."""
+    import torch
+    g = torch.Generator(device=device).manual_seed(seed)
+    out = []
+    for _ in range(count):
+        s = torch.full((p.rows, p.topk), -1, dtype=torch.int32, device=device)
+        for r in range(p.rows):
+            b = int(p.row_bound[r])
+            n = min(b, p.topk)
+            if n:
+                s[r, :n] = torch.randperm(b, generator=g, device=device)[:n].to(torch.int32)
+        out.append(s)
+    return out

@@ -223,7 +223,7 @@ def test_attention_argument_errors(lib):
     ok = fk.make_problem(rows=4, num_pages=16, pt_rows=1, pt_stride=16, max_bound=1024, topk=2048)
     n = ctypes.c_size_t(0)
     assert lib.fp8idx_attention_workspace_size(ctypes.byref(ok), ctypes.byref(n)) == 0
-    # 4 rows: 32 splits of 64 keys; partial outputs 4*32*16*512 fp32 + maxima and sums
+    # 4 rows: 32 splits of 64 entries (4 waves x 16); partial outputs 4*32*16*512 fp32 + maxima and sums
     assert n.value == 4 * 32 * 16 * 512 * 4 + 4 * 32 * 2 * 16 * 4
     assert lib.fp8idx_attention_workspace_size(ctypes.byref(ok), None) == -1
     one = fk.make_problem(rows=1000, num_pages=16, pt_rows=1, pt_stride=16, max_bound=1024, topk=2048)
