@@ -73,14 +73,28 @@ __device__ uint32_t merge_scan(uint32_t v, uint32_t *wsum, uint32_t &total) {
     return off + pre;
 }
 
+// Wave-wide reductions of a 32-bit value (every lane gets the result):
+// shuffles within each 16-lane row, then the rows through permlane swaps.
+template <typename F>
+__device__ __forceinline__ uint32_t merge_wave_reduce(uint32_t v, F op) {
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) v = op(v, (uint32_t)__shfl_xor((int)v, o));
+    const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    v = op(a[0], a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return op(b[0], b[1]);
+}
+
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(int n, int k, const float *cand_score,
                                                               const int32_t *cand_idx, int32_t *out_idx) {
-    __shared__ uint32_t hist[kMergeBins];
-    __shared__ uint32_t wsum[kMergeThreads / 64], wsum2[kMergeThreads / 64];   // one per scan
-    __shared__ uint64_t wmin[kMergeThreads / 64], wmax[kMergeThreads / 64];
+    constexpr int kW = kMergeThreads / 64;
+    __shared__ uint32_t hist[2][kMergeBins];   // pass p counts into hist[p & 1]
+    __shared__ uint32_t wred[3][kW];           // per wave: valid keys, lowest and highest score key
+    __shared__ uint32_t wsum[kW], wsum2[kW];   // per-wave scan totals
     __shared__ uint32_t s_bin, s_above, s_cnt;
     static_assert(kMergePer <= 16, "merge: a thread's counts fit the five-bit scan");
-    const int r = blockIdx.x, t = threadIdx.x, lane = t & 63;
+    static_assert(kMergeBins == 2 * kMergeThreads, "two bins per thread in the bin search");
+    const int r = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const float *sc = cand_score + (int64_t)r * n;
     const int32_t *ix = cand_idx + (int64_t)r * n;
 
@@ -90,7 +104,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(int n, int k, cons
     // (n is a multiple of 16 and the arrays 16-byte aligned: four 16-byte
     // loads per array, all issued before any is used)
     uint64_t key[kMergePer];
-    uint32_t valid = 0;
+    uint32_t valid = 0, lo_hi = 0xFFFFFFFFu, hi_hi = 0u;
     {
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
         u32x4 vi[kMergePer / 4], vs[kMergePer / 4];
@@ -100,100 +114,98 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(int n, int k, cons
         for (int q = 0; q < kMergePer / 4; ++q) vi[q] = *(const u32x4 *)(ix + base + 4 * q);
 #pragma unroll
         for (int q = 0; q < kMergePer / 4; ++q) vs[q] = *(const u32x4 *)(sc + base + 4 * q);
+        // both histograms start at zero (hist[1] is cleared again during
+        // every pass that uses hist[0], and the other way round)
+        for (int i = t; i < 2 * kMergeBins; i += kMergeThreads) (&hist[0][0])[i] = 0u;
 #pragma unroll
         for (int m = 0; m < kMergePer; ++m) {
             const int32_t id = here ? (int32_t)vi[m >> 2][m & 3] : -1;
-            const float f = __uint_as_float(vs[m >> 2][m & 3]);
-            key[m] = id >= 0 ? ((uint64_t)radix_key(f) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)id) : 0ull;
+            const uint32_t rk = radix_key(__uint_as_float(vs[m >> 2][m & 3]));
+            key[m] = id >= 0 ? ((uint64_t)rk << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)id) : 0ull;
             valid += id >= 0;
+            lo_hi = id >= 0 && rk < lo_hi ? rk : lo_hi;
+            hi_hi = id >= 0 && rk > hi_hi ? rk : hi_hi;
         }
     }
-    uint32_t total_valid;   // the row's valid candidates
-    (void)merge_scan(valid, wsum, total_valid);
+    // one exchange for the three row-wide values
+    valid = merge_wave_reduce(valid, [](uint32_t x, uint32_t y) { return x + y; });
+    lo_hi = merge_wave_reduce(lo_hi, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+    hi_hi = merge_wave_reduce(hi_hi, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+    if (lane == 0) { wred[0][wave] = valid; wred[1][wave] = lo_hi; wred[2][wave] = hi_hi; }
+    __syncthreads();
+    uint32_t total_valid = 0;
+    lo_hi = 0xFFFFFFFFu;
+    hi_hi = 0u;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+        total_valid += wred[0][w];
+        lo_hi = wred[1][w] < lo_hi ? wred[1][w] : lo_hi;
+        hi_hi = wred[2][w] > hi_hi ? wred[2][w] : hi_hi;
+    }
     const uint32_t want = total_valid < (uint32_t)k ? total_valid : (uint32_t)k;
 
     // The candidates are the shards' top-k: their scores crowd into a narrow
     // band, so the top bits of the keys are nearly all equal and a first digit
     // taken there would send every atomic to a handful of bins.  The select
-    // runs on the offset key (key - min over the row's valid keys, + 1), whose
-    // first digit starts at the top bit of the range; the order is the same.
-    uint64_t kmin = ~0ull, kmax = 0ull;
-#pragma unroll
-    for (int m = 0; m < kMergePer; ++m)
-        if (key[m] != 0ull) { kmin = key[m] < kmin ? key[m] : kmin; kmax = key[m] > kmax ? key[m] : kmax; }
-    for (int off = 32; off > 0; off >>= 1) {
-        const uint64_t a = __shfl_xor(kmin, off), b = __shfl_xor(kmax, off);
-        kmin = a < kmin ? a : kmin;
-        kmax = b > kmax ? b : kmax;
-    }
-    if (lane == 0) { wmin[t >> 6] = kmin; wmax[t >> 6] = kmax; }
-    __syncthreads();
-    kmin = ~0ull; kmax = 0ull;
-    for (int w = 0; w < kMergeThreads / 64; ++w) {
-        kmin = wmin[w] < kmin ? wmin[w] : kmin;
-        kmax = wmax[w] > kmax ? wmax[w] : kmax;
-    }
+    // runs on the offset key (key - (lowest score key << 32) + 1), whose first
+    // digit starts at the top bit of the range; the order is the same.
+    const uint64_t kmin = (uint64_t)lo_hi << 32;
 #pragma unroll
     for (int m = 0; m < kMergePer; ++m) key[m] = key[m] != 0ull ? key[m] - kmin + 1 : 0ull;   // valid keys stay > 0
-    const int top = kmax >= kmin ? 64 - __clzll((long long)(kmax - kmin + 1)) : 1;   // bits of the offset keys
+    const uint64_t range = ((uint64_t)(hi_hi - lo_hi) << 32) + 0x100000000ull;   // above every offset key
+    const int top = total_valid ? 64 - __clzll((long long)range) : 1;
 
     // Radix select of the want-th largest offset key, 11 bits at a time from
     // the top of the range, over the keys that share the prefix found so far.
-    // Wave 0 finds the bin: lane l sums bins 2047-32l down to 2016-32l, a wave
-    // scan gives the keys in higher bins, the lane holding the want-th key
-    // walks its 32 bins.  The select stops as soon as the remaining need
-    // equals the count of the chosen bin (keys are distinct, so the last
-    // digit always ends it).
+    // Thread t sums bins 2047-2t and 2046-2t; a workgroup scan of those sums
+    // from the top bin down gives the keys in higher bins, and the thread
+    // whose pair holds the want-th key names the bin.  The select stops as
+    // soon as the remaining need equals the count of the chosen bin (keys are
+    // distinct, so the last digit always ends it).  Three barriers per pass.
     uint64_t prefix = 0, pmask = 0;
     uint32_t need = want;
     if (want > 0 && want < total_valid) {
-        for (int shift = top - kMergeBits; ; shift -= kMergeBits) {
+        for (int shift = top - kMergeBits, pass = 0; ; shift -= kMergeBits, ++pass) {
             const int sh = shift < 0 ? 0 : shift;
             const int bits = shift < 0 ? kMergeBits + shift : kMergeBits;
             const uint64_t dmask = ((uint64_t)1 << bits) - 1;
-            for (int i = t; i < kMergeBins; i += kMergeThreads) hist[i] = 0;
-            __syncthreads();
+            uint32_t *h = hist[pass & 1];
 #pragma unroll
             for (int m = 0; m < kMergePer; ++m)
                 if (key[m] != 0ull && (key[m] & pmask) == prefix)
-                    atomicAdd(&hist[(key[m] >> sh) & dmask], 1u);
+                    atomicAdd(&h[(key[m] >> sh) & dmask], 1u);
             __syncthreads();
-            if (t < 64) {
-                const int hi = kMergeBins - 1 - 32 * lane;   // this lane's bins: hi, hi-1, ..., hi-31
-                uint32_t hv[32];
-                uint32_t mine = 0;
+            const int b_hi = kMergeBins - 1 - 2 * t;
+            const uint32_t c_hi = h[b_hi], c_lo = h[b_hi - 1];
+            uint32_t *hn = hist[(pass + 1) & 1];   // the next pass's counters
+            hn[b_hi] = 0u;
+            hn[b_hi - 1] = 0u;
+            const uint32_t c = c_hi + c_lo;
+            uint32_t incl = c;
 #pragma unroll
-                for (int j = 0; j < 32; ++j) { hv[j] = hist[hi - j]; mine += hv[j]; }
-                uint32_t incl = mine;
-                for (int off = 1; off < 64; off <<= 1) {
-                    const uint32_t y = __shfl_up(incl, off);
-                    if (lane >= off) incl += y;
-                }
-                const uint32_t before = incl - mine;
-                if (before < need && need <= incl) {   // walk the counts in registers
-                    uint32_t cum = before;
-                    int jb = 31;
-                    uint32_t ab = 0, cb = 0;
-                    bool found = false;
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t y = (uint32_t)__shfl_up((int)incl, off);
+                if (lane >= off) incl += y;
+            }
+            if (lane == 63) wsum[wave] = incl;
+            __syncthreads();
+            uint32_t before = incl - c;
 #pragma unroll
-                    for (int j = 0; j < 32; ++j) {
-                        const bool here = !found && cum + hv[j] >= need;
-                        jb = here ? j : jb;
-                        ab = here ? cum : ab;
-                        cb = here ? hv[j] : cb;
-                        found = found || here;
-                        cum += hv[j];
-                    }
-                    s_bin = hi - jb; s_above = ab; s_cnt = cb;
-                }
+            for (int w = 0; w < kW; ++w) before += w < wave ? wsum[w] : 0u;
+            if (before < need && need <= before + c) {   // exactly one thread
+                const bool upper = before + c_hi >= need;
+                s_bin = upper ? b_hi : b_hi - 1;
+                s_above = upper ? before : before + c_hi;
+                s_cnt = upper ? c_hi : c_lo;
             }
             __syncthreads();
             need -= s_above;
             prefix |= (uint64_t)s_bin << sh;
             pmask |= dmask << sh;
-            const bool done = s_cnt == need || sh == 0;
-            __syncthreads();
-            if (done) break;
+            if (s_cnt == need || sh == 0) break;
+            // (s_bin, s_above, s_cnt and wsum are written again only after
+            // the next pass's second barrier, which every thread reaches
+            // after reading them here)
         }
     }
     // The selected keys (masked top bits at or above the prefix; all valid
