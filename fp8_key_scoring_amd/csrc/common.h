@@ -32,6 +32,13 @@ constexpr int kSliceCap = kMaxTopk + kCandSlice;    // entries (sure keys + cand
 constexpr int kCandCap = 4096;                      // candidates one row may have (else fallback)
 constexpr int kEntCap = kMaxTopk + kCandCap;        // entries of one row finalize holds
 constexpr int kTieCap = 1024;                       // keys in the third-digit bin finalize ranks
+// Heavy ties (the threshold's third-digit bin holds more keys than finalize
+// ranks): the last 10 bits of the keys in that bin are counted by up to
+// kFbMaxWgs workgroups per row, each over its share of the row
+constexpr int kFbBits = 10;
+constexpr int kFbBins = 1 << kFbBits;
+constexpr int kFbMaxWgs = 8;
+constexpr int64_t kFbKeysPerWg = 65536;
 constexpr int kZeroRows = 256;     // rows the zero block is laid out for (at least)
 constexpr int kDigit1Bits = 6;      // first radix digit (counted while scoring)
 constexpr int kDigit2Bits = 8;      // second radix digit
@@ -74,6 +81,8 @@ struct WsLayout {
     size_t hist1;      // u32 [rz][kHist1Slots][64]  first-digit counts
     size_t hist2;      // u32 [rz][kHist2Slots][256]  second-digit counts inside the first-digit bin
     size_t hist3;      // u32 [rz][256]     third-digit counts of the candidates
+    size_t fb_hist;    // u32 [rz][1024]    heavy-tie fallback: last-10-bit counts of the threshold bin
+    size_t fb_cnt;     // u32 [rz]          finalize workgroups of the row that are done
     size_t state;      // RowState [rows]
     size_t ent_cnt;    // u32 [rows][sel_wgs]              entries (sure keys + candidates) per gather workgroup
     size_t cand_cnt;   // u32 [rows][sel_wgs]              candidates among them
@@ -81,6 +90,7 @@ struct WsLayout {
     size_t scores;     // f32 [rows][sstride]  (only when the caller gives none)
     size_t total;
     int sel_wgs;
+    int fb_wgs;        // finalize workgroups per row (1 .. kFbMaxWgs)
     int64_t sel_chunk;
     int64_t sstride;
 };
@@ -106,6 +116,15 @@ inline WsLayout ws_layout(int rows, int max_bound, bool own_scores, int zero_row
     L.hist1 = take(rz * kHist1Slots * kBins1 * 4);
     L.hist2 = take(rz * kHist2Slots * kBins2 * 4);
     L.hist3 = take(rz * kBins3 * 4);
+    L.fb_hist = take(rz * kFbBins * 4);
+    L.fb_cnt = take(rz * 4);
+    // finalize workgroups per row: one per 64K keys, at most kFbMaxWgs, and
+    // about 256 in all (more would need a second round on the chip, and only
+    // rows with heavy ties use them)
+    int64_t fw = (mb + kFbKeysPerWg - 1) / kFbKeysPerWg;
+    const int64_t cap = rows > 0 ? 256 / rows : 1;
+    if (fw > cap) fw = cap;
+    L.fb_wgs = (int)(fw < 1 ? 1 : (fw > kFbMaxWgs ? kFbMaxWgs : fw));
     L.state = take((size_t)rows * sizeof(RowState));
     L.ent_cnt = take((size_t)rows * n * 4);
     L.cand_cnt = take((size_t)rows * n * 4);

@@ -368,54 +368,47 @@ __global__ __launch_bounds__(kSelThreads) void gather_kernel(SelectArgs a) {
 // ties at T (ascending index), each thread taking 32 consecutive keys, and
 // stops once the row's output is complete.  Both passes keep eight 16-byte
 // loads per thread in flight (32K keys per workgroup step).
-__device__ void fallback_write(const float *row, int b, uint32_t T14, uint32_t need, int32_t *out_row, int k,
-                               const uint32_t *h3, uint32_t *h10, int *sB, uint32_t *sAbove, uint32_t *wsum) {
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    constexpr int kLow = 10;                        // bits below the 22-bit prefix
-    constexpr uint32_t kNone = 0xFFFFFFFFu;
-    for (int i = t; i < (1 << kLow); i += kSelThreads) h10[i] = 0;
-    if (t == 0) { *sB = 0; *sAbove = 0; }
-    __syncthreads();
-    if (t < 64) wave_find_bin(h3, kBins3 / 64, need, lane, sB, sAbove);
-    __syncthreads();
-    const uint32_t T22 = (T14 << kDigit3Bits) | (uint32_t)(*sB);
-    const uint32_t need2 = need - *sAbove;
-    __syncthreads();
-    if (t == 0) { *sB = 0; *sAbove = 0; }
-    // the last 10 bits of the keys with prefix T22: each step 8 x 16-byte
-    // loads per thread (32K keys), all issued before any is used
-    constexpr int kFbVec = 8;
-    constexpr int64_t kFbStep = (int64_t)kFbVec * 4 * kSelThreads;
-    // A step's keys into registers, every load issued before any is used:
-    // 16-byte loads when the whole step lies below the bound and the row is
-    // 16-byte aligned (a caller's score rows need only be 4-byte aligned),
-    // else 4-byte loads at clamped positions (callers test the position).
-    // idx(j) is the first of the four keys of load j.
+// Heavy-tie fallback, part 1: adds to h10 (LDS, kFbBins counters) the last
+// 10 bits of every key in [s0, s1) whose top 22 bits are T22.  Each step
+// loads 8 x 16 bytes per thread (32K keys), all issued before any is used.
+constexpr int kFbVec = 8;
+constexpr int64_t kFbStep = (int64_t)kFbVec * 4 * kSelThreads;
+// A step's keys into registers, every load issued before any is used:
+// 16-byte loads when the whole step lies below `end` and the row is 16-byte
+// aligned (a caller's score rows need only be 4-byte aligned), else 4-byte
+// loads at clamped positions (callers test the position).  idx(j) is the
+// first of the four keys of load j.
+template <typename Idx>
+__device__ __forceinline__ void fb_step_keys(const float *row, int64_t base, int64_t end, Idx idx,
+                                             uint32_t (&u)[kFbVec][4]) {
     const bool al16 = ((uintptr_t)row & 15) == 0;
-    auto step_keys = [&](int64_t base, auto idx, uint32_t (&u)[kFbVec][4]) {
-        if (al16 && base + kFbStep <= b) {   // (uniform)
+    if (al16 && base + kFbStep <= end) {   // (uniform)
 #pragma unroll
-            for (int j = 0; j < kFbVec; ++j) {
-                const u32x4_t v = *(const u32x4_t *)(row + idx(j));
-                u[j][0] = v[0]; u[j][1] = v[1]; u[j][2] = v[2]; u[j][3] = v[3];
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < kFbVec; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int64_t sj = idx(j) + e;
-                    u[j][e] = __float_as_uint(row[sj < b ? sj : b - 1]);
-                }
+        for (int j = 0; j < kFbVec; ++j) {
+            const u32x4_t v = *(const u32x4_t *)(row + idx(j));
+            u[j][0] = v[0]; u[j][1] = v[1]; u[j][2] = v[2]; u[j][3] = v[3];
         }
+    } else {
 #pragma unroll
-        for (int j = 0; j < kFbVec; ++j)   // raw bits -> radix keys, in place
+        for (int j = 0; j < kFbVec; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) u[j][e] = radix_key(__uint_as_float(u[j][e]));
-    };
+            for (int e = 0; e < 4; ++e) {
+                const int64_t sj = idx(j) + e;
+                u[j][e] = __float_as_uint(row[sj < end ? sj : end - 1]);
+            }
+    }
+#pragma unroll
+    for (int j = 0; j < kFbVec; ++j)   // raw bits -> radix keys, in place
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[j][e] = radix_key(__uint_as_float(u[j][e]));
+}
+
+__device__ __forceinline__ void fallback_count(const float *row, int64_t s0, int64_t s1, uint32_t T22, uint32_t *h10) {
+    const int t = threadIdx.x;
+    constexpr uint32_t kNone = 0xFFFFFFFFu;
     uint32_t u[kFbVec][4];
-    for (int64_t base = 0; base < b; base += kFbStep) {
-        step_keys(base, [&](int j) { return base + ((int64_t)j * kSelThreads + t) * 4; }, u);
+    for (int64_t base = s0; base < s1; base += kFbStep) {
+        fb_step_keys(row, base, s1, [&](int j) { return base + ((int64_t)j * kSelThreads + t) * 4; }, u);
         // runs of equal digits within a thread's keys are added at once (ties
         // are the case here, and adds to one LDS word serialize)
         uint32_t run_d = kNone, run_n = 0;
@@ -425,8 +418,8 @@ __device__ void fallback_write(const float *row, int b, uint32_t T14, uint32_t n
             for (int e = 0; e < 4; ++e) {
                 const int64_t s = base + ((int64_t)j * kSelThreads + t) * 4 + e;
                 const uint32_t uk = u[j][e];
-                if (s < b && (uk >> kLow) == T22) {
-                    const uint32_t d = uk & ((1u << kLow) - 1);
+                if (s < s1 && (uk >> kFbBits) == T22) {
+                    const uint32_t d = uk & (kFbBins - 1);
                     if (d != run_d) {
                         if (run_n) atomicAdd(&h10[run_d], run_n);
                         run_d = d;
@@ -437,17 +430,21 @@ __device__ void fallback_write(const float *row, int b, uint32_t T14, uint32_t n
             }
         if (run_n) atomicAdd(&h10[run_d], run_n);
     }
-    __syncthreads();
-    if (t < 64) wave_find_bin(h10, (1 << kLow) / 64, need2, lane, sB, sAbove);
-    __syncthreads();
-    const uint32_t T = (T22 << kLow) | (uint32_t)(*sB);   // the k-th largest key
-    const uint32_t need3 = need2 - *sAbove;              // ties at T to take (lowest indices)
-    // output pass: thread t takes the 32 consecutive keys base + 32t ..
-    // base + 32t + 31 (eight 16-byte loads)
+}
+
+// Part 2 (one workgroup): with T the k-th largest key and need3 the keys
+// equal to T to take, writes the row's selection in ascending index order:
+// thread t takes the 32 consecutive keys base + 32t .. base + 32t + 31 of
+// each step, exclusive prefixes over the workgroup of the tie and the
+// greater-than counts place them; stops once k keys are out.
+__device__ __forceinline__ void fallback_output(const float *row, int b, uint32_t T, uint32_t need3, int32_t *out_row, int k,
+                                uint32_t *wsum) {
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    uint32_t u[kFbVec][4];
     uint32_t sel_run = 0, tie_run = 0;
     for (int64_t base = 0; base < b && sel_run < (uint32_t)k; base += kFbStep) {
         const int64_t s0 = base + (int64_t)kFbVec * 4 * t;
-        step_keys(base, [&](int j) { return s0 + 4 * j; }, u);
+        fb_step_keys(row, base, (int64_t)b, [&](int j) { return s0 + 4 * j; }, u);
         uint32_t ngt = 0, ntie = 0;
 #pragma unroll
         for (int j = 0; j < kFbVec; ++j)
@@ -501,12 +498,19 @@ __device__ void fallback_write(const float *row, int b, uint32_t T14, uint32_t n
 }
 
 // -------------------------------------------------------------- finalize
-// One workgroup per row.  The slices' entries (sure keys and candidates, each
+// Workgroup 0 of a row: the slices' entries (sure keys and candidates, each
 // slice in ascending index, slices in index order) are gathered into LDS in
 // one ascending list; the third digit's bin of the k-th key splits the
 // candidates once more (all above it are taken, the few inside it ranked by
 // key desc, index asc); a stable compaction of the kept entries is the row's
-// output in ascending index order.  The row's histograms are left zeroed.
+// output in ascending index order.
+// Heavy ties (candidates past the slices' capacity, or more keys in the
+// third-digit bin than it ranks): every workgroup of the row (L.fb_wgs, each
+// deciding so from the same counts) counts the last 10 bits of the bin's keys
+// over its share of the row into the row's global counters; the last one to
+// arrive finds the k-th key and writes the selection.  Every workgroup of the
+// row arrives at a counter; the last one leaves the row's histograms and
+// counters zeroed, after every read of them.
 __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
     __shared__ unsigned long long ent[kEntCap];   // the row's entries, ascending index
     __shared__ unsigned long long tie[kTieCap];   // candidates inside the third-digit bin
@@ -514,14 +518,15 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
     __shared__ uint32_t roff[kSelMaxWgs + 1];    // exclusive prefix of the entries past 16*kPre per slice
     __shared__ uint32_t h3[kBins3];
     __shared__ uint32_t wsum[kWaves], wsum2[2 * kWaves];
-    __shared__ int sB;
-    __shared__ uint32_t sAbove, ntie, ovf;
+    __shared__ int sB, sB10;
+    __shared__ uint32_t sAbove, sAbove10, ntie, ovf, s_ticket, s_late;
     constexpr int kPer = kEntCap / kSelThreads;   // entries per thread
     constexpr int kPre = 4;                       // entries per thread loaded ahead of the counts
     static_assert(kPer < 8, "finalize: a thread's kept count fits the three-bit scan");
     static_assert(kEntCap % kSelThreads == 0, "finalize: whole entries per thread");
     static_assert(kSelMaxWgs * 16 == kSelThreads, "finalize: 16 threads per slice");
-    const int r = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int xw = blockIdx.x, r = blockIdx.y, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int nfb = a.L.fb_wgs;
     const int k = a.topk;
     const int S = a.L.sel_wgs;
     int32_t *out_row = a.out_idx + (int64_t)r * k;
@@ -546,6 +551,8 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
     for (int m = 0; m < kPre; ++m) pre[m] = sl[(int64_t)xs * kSliceCap + j0 + 16 * m];
     __builtin_amdgcn_sched_barrier(0);
     const int b = clamp_bound(b_raw, a.max_bound);
+    bool overflow = false;        // heavy ties: the row takes the fallback
+    uint32_t T22 = 0, need2 = 0;  // the k-th key's top 22 bits, keys to take inside that bin
     if (b > k) {
         // slices that start at or past the bound were not written: empty
         const bool live = lane < S && (int64_t)lane * a.L.sel_chunk < b;
@@ -574,12 +581,18 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
             }
         }
         if (t < kBins3) h3[t] = h3v;
-        if (t == 0) { sB = 0; sAbove = 0; ntie = 0; }
+        if (t == 0) { sB = 0; sAbove = 0; ntie = 0; s_late = 0; }
+        __syncthreads();
+        // the third-digit bin of the k-th key and the keys in it: the same
+        // decision in every workgroup of the row
+        if (t < 64) wave_find_bin(h3, kBins3 / 64, (uint32_t)need, lane, &sB, &sAbove);
         __syncthreads();
         const int N = (int)offe[kSelMaxWgs];
-        bool overflow = ovf != 0u;
+        overflow = ovf != 0u || h3[sB] > (uint32_t)kTieCap;
+        T22 = (T14 << kDigit3Bits) | (uint32_t)sB;
+        need2 = (uint32_t)need - sAbove;
         unsigned long long e[kPer];
-        if (!overflow) {
+        if (!overflow && xw == 0) {
             if (x < S) {
                 const int o = (int)offe[x], n = (int)(offe[x + 1] - offe[x]);
 #pragma unroll
@@ -613,9 +626,7 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
                 for (int m = 0; m < kPer; ++m)
                     if (dst[m] >= 0) ent[dst[m]] = v[m];
             }
-            if (t < 64) wave_find_bin(h3, kBins3 / 64, (uint32_t)need, lane, &sB, &sAbove);
             __syncthreads();
-            const uint32_t T22 = (T14 << kDigit3Bits) | (uint32_t)sB;
             // this thread's entries t*kPer .. t*kPer+kPer-1; candidates in the
             // third-digit bin are collected for ranking
 #pragma unroll
@@ -630,11 +641,14 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
                 }
             }
             __syncthreads();
-            overflow = ntie > (uint32_t)kTieCap;
+            // (more ties than the bin's count only with counters left dirty
+            // by a misused workspace: this workgroup then counts the whole
+            // row alone, below)
+            if (t == 0 && ntie > (uint32_t)kTieCap) s_late = 1;
+            __syncthreads();
         }
-        if (!overflow) {
-            const uint32_t T22 = (T14 << kDigit3Bits) | (uint32_t)sB;
-            const uint32_t need3 = (uint32_t)need - sAbove;
+        if (!overflow && xw == 0 && !s_late) {
+            const uint32_t need3 = need2;
             const int nt = (int)ntie;
             bool kept[kPer];
             uint32_t cnt = 0;
@@ -668,15 +682,67 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
                     if (pos < (uint32_t)k) out_row[pos] = (int32_t)((uint32_t)e[q] & 0x7FFFFFFFu);
                     ++pos;
                 }
-        } else {
-            fallback_write(a.scores + (int64_t)r * a.sstride, b, T14, (uint32_t)need, out_row, k, h3,
-                           (uint32_t *)ent, &sB, &sAbove, wsum2);
+        } else if (overflow || (xw == 0 && s_late)) {
+            // the last 10 bits of the bin's keys over this workgroup's share
+            // (the whole row when it counts alone), into LDS
+            const bool alone = !overflow;   // (the late case: workgroup 0 only)
+            int64_t share = ((int64_t)b + nfb - 1) / nfb;
+            share = (share + kFbStep - 1) / kFbStep * kFbStep;
+            const int64_t s0 = alone ? 0 : min((int64_t)xw * share, (int64_t)b);
+            const int64_t s1 = alone ? (int64_t)b : min(s0 + share, (int64_t)b);
+            uint32_t *h10 = (uint32_t *)ent;
+            for (int i = t; i < kFbBins; i += kSelThreads) h10[i] = 0;
+            __syncthreads();
+            fallback_count(a.scores + (int64_t)r * a.sstride, s0, s1, T22, h10);
+            __syncthreads();
+            if (!alone && nfb > 1) {   // into the row's counters (device-scope atomics)
+                uint32_t *g10 = (uint32_t *)(a.ws + a.L.fb_hist) + (int64_t)r * kFbBins;
+                for (int i = t; i < kFbBins; i += kSelThreads)
+                    if (h10[i]) __hip_atomic_fetch_add(&g10[i], h10[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (alone) {
+                if (t < 64) wave_find_bin(h10, kFbBins / 64, need2, lane, &sB10, &sAbove10);
+                __syncthreads();
+                fallback_output(a.scores + (int64_t)r * a.sstride, b, (T22 << kFbBits) | (uint32_t)sB10,
+                                need2 - sAbove10, out_row, k, wsum2);
+            }
         }
+    }
+    // ---- every workgroup of the row arrives; the last one finishes the
+    // heavy-tie case and clears the row's counters.  No fence: the counts go
+    // in with device-scope atomics, each thread waits until its own are
+    // performed, and the ticket is a device-scope atomic taken after that;
+    // the last workgroup reads the counts with device-scope atomic loads.  (A
+    // device-scope fence here would write back this XCD's L2.)
+    if (nfb > 1) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (t == 0)
+            s_ticket = __hip_atomic_fetch_add((uint32_t *)(a.ws + a.L.fb_cnt) + r, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (s_ticket != (uint32_t)nfb - 1) return;
+    }
+    if (b > k && overflow) {
+        uint32_t *h10 = (uint32_t *)ent;
+        if (nfb > 1) {
+            uint32_t *g10 = (uint32_t *)(a.ws + a.L.fb_hist) + (int64_t)r * kFbBins;
+            for (int i = t; i < kFbBins; i += kSelThreads) {
+                h10[i] = __hip_atomic_load(&g10[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                g10[i] = 0;
+            }
+        }
+        __syncthreads();
+        if (t < 64) wave_find_bin(h10, kFbBins / 64, need2, lane, &sB10, &sAbove10);
+        __syncthreads();
+        fallback_output(a.scores + (int64_t)r * a.sstride, b, (T22 << kFbBits) | (uint32_t)sB10,
+                        need2 - sAbove10, out_row, k, wsum2);
     }
     if (t < kHist1Slots * kBins1) ((uint32_t *)(a.ws + a.L.hist1))[(int64_t)r * kHist1Slots * kBins1 + t] = 0;
     for (int i = t; i < kHist2Slots * kBins2; i += kSelThreads)
         ((uint32_t *)(a.ws + a.L.hist2))[(int64_t)r * kHist2Slots * kBins2 + i] = 0;
     if (t < kBins3) hist3[t] = 0;
+    if (t == 0 && nfb > 1) ((uint32_t *)(a.ws + a.L.fb_cnt))[r] = 0;
 }
 
 __global__ void fill_zero_kernel(uint32_t *p, size_t n) {
@@ -700,7 +766,7 @@ hipError_t launch_gather(const SelectArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_finalize(const SelectArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL(finalize_kernel, dim3(a.rows), dim3(kSelThreads), 0, st, a);
+    hipLaunchKernelGGL(finalize_kernel, dim3(a.L.fb_wgs, a.rows), dim3(kSelThreads), 0, st, a);
     return hipGetLastError();
 }
 

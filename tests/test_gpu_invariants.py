@@ -156,12 +156,13 @@ def test_validate_reports_each_kind_of_bad_array():
 
 
 def _zero_block_bytes(rows):
-    """Bytes of the workspace's zero block (the three digit histograms), the
-    part every launch must find zero and leaves zero; the rest is scratch a
-    launch writes before it reads (sizes as the library lays them out)."""
+    """Bytes of the workspace's zero block (the three digit histograms, the
+    heavy-tie counters and the finalize arrival counters), the part every
+    launch must find zero and leaves zero; the rest is scratch a launch
+    writes before it reads (sizes as the library lays them out)."""
     al = lambda x: (x + 255) // 256 * 256
     rz = max(rows, 256)
-    return al(rz * 16 * 64 * 4) + al(rz * 8 * 256 * 4) + al(rz * 256 * 4)
+    return al(rz * 16 * 64 * 4) + al(rz * 8 * 256 * 4) + al(rz * 256 * 4) + al(rz * 1024 * 4) + al(rz * 4)
 
 
 def test_poisoned_scratch_gives_the_same_bytes():
@@ -181,3 +182,38 @@ def test_poisoned_scratch_gives_the_same_bytes():
             _, o = run_launch(p, keep_scores=False, workspace=ws)
             assert np.array_equal(o, ref)
             assert not ws[:z].any()            # the zero block is left zero
+
+
+def test_heavy_tie_rows_leave_the_workspace_clean():
+    # rows whose threshold bin overflows the ranked ties: several finalize
+    # workgroups per row count the bin's last digits, the last one to arrive
+    # writes the selection and clears the row's counters.  Two launches on
+    # one workspace give the same bytes, the zero block (histograms, heavy-tie
+    # counters, arrival counters) is zero after each, and a normal problem on
+    # the same workspace afterwards is unaffected.
+    import oracle
+    say("[gpu] heavy-tie rows: workspace left clean")
+    rng = np.random.default_rng(41)
+    n = 300000                                  # five finalize workgroups per row
+    vals = np.array([1.0, np.nextafter(np.float32(1.0), np.float32(2.0))], np.float32)
+    rows = np.stack([vals[rng.integers(0, 2, size=n)] for _ in range(3)]).astype(np.float32)
+    rows[1, rng.choice(n, 700, replace=False)] = 4.0
+    bounds = np.array([n, n - 1, 123457], np.int32)
+    sc = torch.from_numpy(rows).to("cuda:0")
+    rb = torch.from_numpy(bounds).to("cuda:0")
+    prob = fk.make_problem(rows=3, num_pages=1, pt_rows=1, pt_stride=(n + 63) // 64, max_bound=n, topk=2048,
+                           score_stride=n)
+    ws = fk.new_workspace(prob, False, "cuda:0")
+    want = [np.sort(oracle.topk(np.ascontiguousarray(rows[r, :bounds[r]]), 2048)) for r in range(3)]
+    for rep in range(2):
+        out = fk.indexer_topk(sc, rb, max_bound=n, workspace=ws).cpu().numpy()
+        torch.cuda.synchronize()
+        for r in range(3):
+            assert np.array_equal(out[r], want[r]), (rep, r)
+        assert not ws[:_zero_block_bytes(3)].any(), "counters left non-zero"
+    p = _prob(42)
+    ref_scores, ref = run_launch(p)
+    d = to_device(p)
+    o = fk.indexer_topk(torch.from_numpy(ref_scores).to("cuda:0"), d["row_bound"], max_bound=p.max_bound,
+                        topk=p.topk, workspace=ws)
+    assert np.array_equal(o.cpu().numpy(), ref)
