@@ -75,12 +75,12 @@ def _group_max(p):
 
 
 def source_sha256():
-    """sha256 over the HIP sources of the scoring and selection kernels: the
-    committed counter summaries carry the value they were taken on."""
+    """sha256 over the HIP sources of the scoring kernel (the kernel whose
+    traffic and MFMA figures the counter summary holds): the committed
+    summaries carry the value they were taken on."""
     import hashlib
     h = hashlib.sha256()
-    for fn in ("fp8_key_scoring_amd/csrc/score.hip", "fp8_key_scoring_amd/csrc/select.hip",
-               "fp8_key_scoring_amd/csrc/common.h"):
+    for fn in ("fp8_key_scoring_amd/csrc/score.hip", "fp8_key_scoring_amd/csrc/common.h"):
         with open(os.path.join(ROOT, fn), "rb") as f:
             h.update(f.read())
     return h.hexdigest()

@@ -218,6 +218,8 @@ hipError_t launch_hist1(const SelectArgs &a, hipStream_t st);
 hipError_t launch_refine(const SelectArgs &a, hipStream_t st);
 hipError_t launch_gather(const SelectArgs &a, hipStream_t st);
 hipError_t launch_finalize(const SelectArgs &a, hipStream_t st);
+// the chain in one workgroup per row (valid when L.sel_wgs == 1 and L.fb_wgs == 1)
+hipError_t launch_select1(const SelectArgs &a, bool with_hist1, hipStream_t st);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
 hipError_t launch_shard_cand(const float *scores, int64_t sstride, const int32_t *out_idx, int rows, int k,
                              int g, int G, float *cand_score, int32_t *cand_idx, hipStream_t st);

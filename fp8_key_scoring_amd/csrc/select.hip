@@ -156,11 +156,11 @@ __device__ __forceinline__ uint32_t hist1_sum(const uint32_t (&c)[kHist1Slots]) 
 // ---------------------------------------------------------------- hist1
 // First-digit histogram of stored scores (used when the scores were not
 // produced by this launch's scoring pass).  One LDS copy per wave.
-__global__ __launch_bounds__(kSelThreads) void hist1_kernel(SelectArgs a) {
+__device__ __forceinline__ void hist1_body(const SelectArgs &a, int x, int r) {
     __shared__ uint32_t h[kWaves][kBins1];
-    const int r = blockIdx.y, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int b = clamp_bound(a.row_bound[r], a.max_bound);
-    const int64_t s0 = (int64_t)blockIdx.x * a.L.sel_chunk;
+    const int64_t s0 = (int64_t)x * a.L.sel_chunk;
     if (s0 >= b) return;
     const int64_t s1 = min(s0 + a.L.sel_chunk, (int64_t)b);
     const float *row = a.scores + (int64_t)r * a.sstride;
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kSelThreads) void hist1_kernel(SelectArgs a) {
     if (t < kBins1) {
         uint32_t c = 0;
         for (int w = 0; w < kWaves; ++w) c += h[w][t];
-        if (c) atomicAdd((uint32_t *)(a.ws + a.L.hist1) + ((int64_t)r * kHist1Slots + blockIdx.x % kHist1Slots) * kBins1 + t, c);
+        if (c) atomicAdd((uint32_t *)(a.ws + a.L.hist1) + ((int64_t)r * kHist1Slots + x % kHist1Slots) * kBins1 + t, c);
     }
 }
 
@@ -187,12 +187,12 @@ __global__ __launch_bounds__(kSelThreads) void hist1_kernel(SelectArgs a) {
 // Four LDS copies (wave % 4) keep the waves' atomics apart; with one copy per
 // wave the zeroing and the final sum over 16 copies cost more than the
 // collisions they avoid (C5's launch 3 us longer).
-__global__ __launch_bounds__(kSelThreads) void refine_kernel(SelectArgs a) {
+__device__ __forceinline__ void refine_body(const SelectArgs &a, int x, int r) {
     __shared__ uint32_t h1[kBins1];
     __shared__ uint32_t h2[4][kBins2];
     __shared__ int sb1;
     __shared__ uint32_t sabove1;
-    const int r = blockIdx.y, x = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int b = clamp_bound(a.row_bound[r], a.max_bound);
     const uint32_t k = (uint32_t)a.topk;
     const int64_t s0 = (int64_t)x * a.L.sel_chunk;
@@ -242,13 +242,13 @@ __global__ __launch_bounds__(kSelThreads) void refine_kernel(SelectArgs a) {
 // Every workgroup of a row derives the same split from the two histograms,
 // writes its sure keys and candidates (each ascending) to its own slices and
 // counts the candidates' third digits.
-__global__ __launch_bounds__(kSelThreads) void gather_kernel(SelectArgs a) {
+__device__ __forceinline__ void gather_body(const SelectArgs &a, int x, int r) {
     __shared__ uint32_t h2[kBins2];
     __shared__ uint32_t h3[kBins3];
     __shared__ uint32_t cs[kSelUnroll * kWaves], cc[kSelUnroll * kWaves];
     __shared__ int sb2;
     __shared__ uint32_t sabove2, tot_s, tot_c;
-    const int r = blockIdx.y, x = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int b = clamp_bound(a.row_bound[r], a.max_bound);
     const int k = a.topk;
     const int S = a.L.sel_wgs;
@@ -511,7 +511,7 @@ __device__ __forceinline__ void fallback_output(const float *row, int b, uint32_
 // arrive finds the k-th key and writes the selection.  Every workgroup of the
 // row arrives at a counter; the last one leaves the row's histograms and
 // counters zeroed, after every read of them.
-__global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
+__device__ __forceinline__ void finalize_body(const SelectArgs &a, int xw, int r) {
     __shared__ unsigned long long ent[kEntCap];   // the row's entries, ascending index
     __shared__ unsigned long long tie[kTieCap];   // candidates inside the third-digit bin
     __shared__ uint32_t offe[kSelMaxWgs + 1];
@@ -525,7 +525,7 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
     static_assert(kPer < 8, "finalize: a thread's kept count fits the three-bit scan");
     static_assert(kEntCap % kSelThreads == 0, "finalize: whole entries per thread");
     static_assert(kSelMaxWgs * 16 == kSelThreads, "finalize: 16 threads per slice");
-    const int xw = blockIdx.x, r = blockIdx.y, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int nfb = a.L.fb_wgs;
     const int k = a.topk;
     const int S = a.L.sel_wgs;
@@ -745,6 +745,40 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
     if (t == 0 && nfb > 1) ((uint32_t *)(a.ws + a.L.fb_cnt))[r] = 0;
 }
 
+__global__ __launch_bounds__(kSelThreads) void hist1_kernel(SelectArgs a) { hist1_body(a, blockIdx.x, blockIdx.y); }
+__global__ __launch_bounds__(kSelThreads) void refine_kernel(SelectArgs a) { refine_body(a, blockIdx.x, blockIdx.y); }
+__global__ __launch_bounds__(kSelThreads) void gather_kernel(SelectArgs a) { gather_body(a, blockIdx.x, blockIdx.y); }
+__global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
+    finalize_body(a, blockIdx.x, blockIdx.y);
+}
+
+// A row that one selection workgroup covers (bound <= one slice, one
+// finalize workgroup): the stages run in one workgroup, one after another,
+// with workgroup barriers where the chain has kernel boundaries.  The stages
+// hand over through the workspace exactly as the separate kernels do (their
+// writes are visible to the workgroup after the barrier); every early exit in
+// them is uniform over the workgroup and comes before its first barrier.
+template <bool kHist1>
+__global__ __launch_bounds__(kSelThreads) void select1_kernel(SelectArgs a) {
+    // (nothing moves across a stage boundary: each stage's values are
+    // computed inside it, which keeps the register peak that of finalize)
+    int r = blockIdx.x;
+    if (kHist1) {
+        hist1_body(a, 0, r);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    refine_body(a, 0, r);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    gather_body(a, 0, r);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    int x0 = 0;   // (opaque, so that finalize compiles as in its own kernel)
+    asm volatile("" : "+s"(r), "+s"(x0));
+    finalize_body(a, x0, r);
+}
+
 __global__ void fill_zero_kernel(uint32_t *p, size_t n) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
         p[i] = 0;
@@ -767,6 +801,14 @@ hipError_t launch_gather(const SelectArgs &a, hipStream_t st) {
 
 hipError_t launch_finalize(const SelectArgs &a, hipStream_t st) {
     hipLaunchKernelGGL(finalize_kernel, dim3(a.L.fb_wgs, a.rows), dim3(kSelThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_select1(const SelectArgs &a, bool with_hist1, hipStream_t st) {
+    if (with_hist1)
+        hipLaunchKernelGGL(select1_kernel<true>, dim3(a.rows), dim3(kSelThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(select1_kernel<false>, dim3(a.rows), dim3(kSelThreads), 0, st, a);
     return hipGetLastError();
 }
 
