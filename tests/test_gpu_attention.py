@@ -131,3 +131,20 @@ def test_attention_many_rows():
         return np.stack([rng.choice(int(b), 2048, replace=False) for b in p.row_bound]).astype(np.int32)
     p, q, kv, sel, sm = _case("attn_many", 64, lens, rows, sel_fn)
     _check(p, q, kv, sel, sm, "64 rows")
+
+
+def test_attention_one_split_per_row_writes_directly():
+    # 300 rows (more than the 256 workgroups a launch aims at): one split per
+    # row, so the attention kernel normalises and writes out and lse itself
+    # (no combine); 320-entry index lists, some rows short of 320 valid keys
+    lens = [400 + 97 * i for i in range(75)]
+    rows = [rw for i, n in enumerate(lens) for rw in syn.verify_rows(i, n)]
+    def sel_fn(p, rng):
+        s = np.full((p.rows, p.topk), -1, np.int32)
+        for r, b in enumerate(p.row_bound):
+            m = min(int(b), p.topk) - (r % 7 == 3) * 50
+            s[r, :m] = rng.choice(int(b), m, replace=False)
+        return s
+    p, q, kv, sel, sm = _case("attn_direct", 65, lens, rows, sel_fn, topk=320)
+    assert p.rows == 300
+    _check(p, q, kv, sel, sm, "one split per row")
