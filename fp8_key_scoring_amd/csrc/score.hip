@@ -94,6 +94,12 @@ __device__ __forceinline__ gptr<T> scalar_ptr(const T *p) {
     return (gptr<T>)v;
 }
 
+// A workgroup barrier for LDS traffic: it waits for this wave's LDS
+// operations only.  __syncthreads() also waits for every global load the wave
+// has in flight, which in the set-up would hold every wave until its whole
+// key ring had arrived.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Sums each of four per-lane partials over the four 16-lane rows and leaves
 // the total of partial q in lane row q (each lane keeps its column): one
 // 32-lane swap round and one 16-lane swap round.
@@ -210,8 +216,16 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
         const int wave_idx = tid >> 6;
         if (!staged) {   // q_slot is 0 here
             stage_q<R>(a, j.row0, tid, lds_q);
-            __syncthreads();
+            lds_barrier();
         }
+        // weights of the D rows a lane holds: heads 16*hb + 4*(lane/16) + jj
+        // (issued ahead of the ring: loads complete in order, and the first
+        // step's epilogue must not wait for the whole ring)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb)
+                wv[r][hb] = *(gptr<f32x4_t>)(a.w + (int64_t)(j.row0 + r) * kHeads + 16 * hb + 4 * lrow) * 0.5f;
 #pragma unroll
         for (int p = 0; p < kRing; ++p) load_group(p, kb[p]);
 #pragma unroll
@@ -221,12 +235,6 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
                     qa[r][hb][ks] = *(const bf16x8_t *)(lds_q + q_lds_off(q_slot + r, 16 * hb + kig, 4 * lrow + ks));
-        // weights of the D rows a lane holds: heads 16*hb + 4*(lane/16) + jj
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int hb = 0; hb < 4; ++hb)
-                wv[r][hb] = *(gptr<f32x4_t>)(a.w + (int64_t)(j.row0 + r) * kHeads + 16 * hb + 4 * lrow) * 0.5f;
         // The linear term's A operand: A row 4p + r holds part p of
         // u_r = (1/2) sum_h w[r][h] q[r][h] (fp32, heads in order), split
         // into three bf16 parts hi + mid + lo (each residual exact in fp32,
@@ -265,19 +273,19 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
                 t1_lds[(ks * 64 + 2 * 4 + ur + 16 * lr) * 8 + (d & 7)] = lo;
             }
         }
-        __syncthreads();
+        lds_barrier();
         const bool t1_row = (kig >> 2) < 3 && (kig & 3) < R;   // this lane's A row is used
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const bf16x8_t v = *(const bf16x8_t *)(t1_lds + (ks * 64 + lane) * 8);
             t1a[ks] = t1_row ? v : bf16x8_t{};
         }
-        __syncthreads();   // t1_lds may be written again by the next row group
+        lds_barrier();   // t1_lds may be written again by the next row group
         if (kHist) {   // every wave is done with q in LDS: the region becomes the counters
             u32x4_t *c4 = (u32x4_t *)lds_cnt;
             const uint32_t z = (uint32_t)tid >> 16;   // 0, built here rather than kept live
             for (int i = tid; i < kHistLds / 4; i += kScoreThreads) c4[i] = u32x4_t{z, z, z, z};
-            __syncthreads();
+            lds_barrier();
         }
     }
     if (j.n_my == 0) return;
@@ -530,7 +538,7 @@ void score_kernel(ScoreArgs a) {
             const int ci = threadIdx.x + c * kScoreThreads;
             *(u32x4_t *)(lds_q + q_lds_off(ci >> 10, (ci >> 4) & 63, ci & 15)) = qt_blk[c];
         }
-        __syncthreads();
+        lds_barrier();   // (the page ids may still be in flight)
     }
 
     for (int bi = bi_first; bi < kGroupRows; ++bi) {
@@ -539,7 +547,7 @@ void score_kernel(ScoreArgs a) {
         else if (!group_at(bi, rg, gmax)) continue;
         const int r0 = yb + bi;
         const int c1 = min(c0 + a.chunk, gmax);
-        if (bi != bi_first) __syncthreads();   // the previous group's write-out is done with LDS
+        if (bi != bi_first) lds_barrier();   // the previous group's write-out is done with LDS
         // the thread index passes through an empty asm per group: what the
         // group's code derives from it (LDS and key offsets) is recomputed in
         // each group instead of being kept live across all of them
@@ -579,7 +587,7 @@ void score_kernel(ScoreArgs a) {
         // ---- add the chunk's first-digit counts to the row totals: wave r
         // sums row r's counters (lane = digit) into copy (workgroup % 16)
         if (kHist) {
-            __syncthreads();
+            lds_barrier();
             const int hr = tid >> 6;   // row slot; lane = digit
             if (hr < rg) {
                 uint32_t c = 0;
