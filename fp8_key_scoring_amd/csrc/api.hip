@@ -102,8 +102,8 @@ int run_select(const fp8idx_problem_t *p, const float *scores, int64_t sstride,
     a.max_bound = p->max_bound;
     a.topk = p->topk;
     hipError_t e = hipSuccess;
-    // rows that one selection workgroup covers: the chain as one kernel
-    if (L.sel_wgs == 1 && L.fb_wgs == 1) return to_code(launch_select1(a, need_hist1, st));
+    // short rows: one kernel, one workgroup per row
+    if (p->max_bound <= kSmallMax) return to_code(launch_select_small(a, need_hist1, st));
     if (need_hist1 && (e = launch_hist1(a, st)) != hipSuccess) return to_code(e);
     if ((e = launch_refine(a, st)) != hipSuccess) return to_code(e);
     if ((e = launch_gather(a, st)) != hipSuccess) return to_code(e);

@@ -32,6 +32,11 @@ constexpr int kSliceCap = kMaxTopk + kCandSlice;    // entries (sure keys + cand
 constexpr int kCandCap = 4096;                      // candidates one row may have (else fallback)
 constexpr int kEntCap = kMaxTopk + kCandCap;        // entries of one row finalize holds
 constexpr int kTieCap = 1024;                       // keys in the third-digit bin finalize ranks
+// Launches whose rows all have at most this many keys select with one
+// workgroup per row that holds the row's keys in registers (16 per thread);
+// past it the multi-workgroup chain is faster (4 rows x 32,768 keys: 27.3
+// against 32.6 us per launch).
+constexpr int kSmallMax = 16384;
 // Heavy ties (the threshold's third-digit bin holds more keys than finalize
 // ranks): the last 10 bits of the keys in that bin are counted by up to
 // kFbMaxWgs workgroups per row, each over its share of the row
@@ -218,8 +223,9 @@ hipError_t launch_hist1(const SelectArgs &a, hipStream_t st);
 hipError_t launch_refine(const SelectArgs &a, hipStream_t st);
 hipError_t launch_gather(const SelectArgs &a, hipStream_t st);
 hipError_t launch_finalize(const SelectArgs &a, hipStream_t st);
-// the chain in one workgroup per row (valid when L.sel_wgs == 1 and L.fb_wgs == 1)
-hipError_t launch_select1(const SelectArgs &a, bool with_hist1, hipStream_t st);
+// rows of at most kSmallMax keys: one workgroup per row (with_hist1: it counts
+// the first digit itself; else it takes, and clears, the scoring pass's counts)
+hipError_t launch_select_small(const SelectArgs &a, bool with_hist1, hipStream_t st);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
 hipError_t launch_shard_cand(const float *scores, int64_t sstride, const int32_t *out_idx, int rows, int k,
                              int g, int G, float *cand_score, int32_t *cand_idx, hipStream_t st);

@@ -752,31 +752,255 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
     finalize_body(a, blockIdx.x, blockIdx.y);
 }
 
-// A row that one selection workgroup covers (bound <= one slice, one
-// finalize workgroup): the stages run in one workgroup, one after another,
-// with workgroup barriers where the chain has kernel boundaries.  The stages
-// hand over through the workspace exactly as the separate kernels do (their
-// writes are visible to the workgroup after the barrier); every early exit in
-// them is uniform over the workgroup and comes before its first barrier.
-template <bool kHist1>
-__global__ __launch_bounds__(kSelThreads) void select1_kernel(SelectArgs a) {
-    // (nothing moves across a stage boundary: each stage's values are
-    // computed inside it, which keeps the register peak that of finalize)
-    int r = blockIdx.x;
-    if (kHist1) {
-        hist1_body(a, 0, r);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
+// ---------------------------------------------------------------------------
+// Rows of at most kSmallMax keys (select_small_kernel): one workgroup per row
+// reads the row's scores once into registers as radix keys (thread t holds
+// keys t + 1024 j, at most 16), finds the k-th largest key T digit by digit
+// in LDS histograms, and writes, in ascending index order, every key above T
+// and the first `need` keys equal to T (exact for any ties; no fallback).
+// Digits: the first (bits 31..26) as everywhere else, from the scoring pass's
+// counts in the workspace (the kernel clears them) or counted here; then bits
+// 25..17, 16..8 and 7..0 (512, 512 and 256 bins) in eight LDS histogram
+// copies (wave % 8), double-buffered so that one is cleared while the other
+// counts.  LDS adds are one per counted key and lane; a wave whose keys share
+// one digit (heavy ties) folds them into one add.  Wave scans use DPP row
+// shifts (a shuffle goes through the LDS crossbar at LDS latency per step).
+// Output: per 1024-key slice, each wave's counts of keys above and equal to T
+// (ballots), one scan of those counts in index order, then every lane writes
+// its selected key at (keys above before it) + min(keys equal before it, need).
+constexpr int kSmallWaves = kSelThreads / 64;
+constexpr int kSmallSlots = kSmallMax / kSelThreads;   // keys per thread
+constexpr int kSmallBins = 512;
+constexpr int kSmallCopies = 8;   // histogram copies (wave % 8)
+static_assert(kSmallSlots * kSmallWaves <= 64 * 8, "the output scan covers 8 counts per lane");
+
+// Inclusive prefix sum over the wave's lanes with DPP row shifts (VALU only;
+// a shuffle goes through the LDS crossbar at LDS latency per step): a
+// Hillis-Steele scan inside each row of 16 lanes, then each row adds the
+// totals of the rows before it.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+    const int row = lane >> 4;
+    return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
+// wave_find_bin for the short-row path (one full wave; h: 64 * PER bins in
+// LDS, PER <= 8): the lane sums and the final walk stay in registers.
+template <int PER>
+__device__ __forceinline__ void wave_find_bin_regs(const uint32_t *h, uint32_t need, int lane, int *outB,
+                                                   uint32_t *outAbove) {
+    uint32_t c[PER], mine = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        c[j] = h[lane * PER + j];
+        mine += c[j];
     }
-    refine_body(a, 0, r);
+    const uint32_t incl = wave_incl_scan(mine, lane);
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    const uint32_t above_lane = total - incl;   // lanes after this one (higher bins)
+    const uint64_t m = __ballot((above_lane < need) & (need <= above_lane + mine));
+    if (m && lane == __ffsll((unsigned long long)m) - 1) {
+        uint32_t cum = above_lane;
+#pragma unroll
+        for (int j = PER - 1; j >= 0; --j) {
+            if (cum + c[j] >= need) {
+                *outB = lane * PER + j;
+                *outAbove = cum;
+                break;
+            }
+            cum += c[j];
+        }
+    }
+}
+
+// Digit counts of up to four distinct digits folded per wave (the first
+// digit: a row's keys share few of them, and same-address LDS atomics of one
+// instruction serialize); the remaining lanes add one by one.
+__device__ __forceinline__ void small_count_folded(uint32_t *h, uint32_t d, bool valid, int lane) {
+    uint64_t todo = __ballot(valid);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        if (!todo) break;
+        const int leader = __ffsll((unsigned long long)todo) - 1;
+        const uint32_t dl = __builtin_amdgcn_readlane(d, leader);
+        const uint64_t m = __ballot(valid & (d == dl)) & todo;
+        if (lane == leader) atomicAdd(h + dl, (uint32_t)__popcll(m));
+        todo &= ~m;
+    }
+    if ((todo >> lane) & 1) atomicAdd(h + d, 1u);
+}
+
+// Digit counts: one add when every counted lane of the wave has the same
+// digit, else one per lane.
+__device__ __forceinline__ void small_count(uint32_t *h, uint32_t d, bool valid, int lane) {
+    const uint64_t act = __ballot(valid);
+    if (!act) return;
+    const int first = __ffsll((unsigned long long)act) - 1;
+    const uint32_t d0 = __builtin_amdgcn_readlane(d, first);
+    if (__ballot(valid & (d == d0)) == act) {
+        if (lane == first) atomicAdd(h + d0, (uint32_t)__popcll(act));
+    } else if (valid) {
+        atomicAdd(h + d, 1u);
+    }
+}
+
+template <bool kHist1>
+__global__ __launch_bounds__(kSelThreads) void select_small_kernel(SelectArgs a) {
+    __shared__ uint32_t shist2[2][kSmallCopies][kSmallBins];   // double-buffered: one is cleared while the other counts
+    __shared__ uint32_t stot[kSmallBins];
+    __shared__ uint32_t scnt[kSmallSlots * kSmallWaves];   // [slice][wave]: above << 16 | equal, then their prefix
+    __shared__ int s_bin;
+    __shared__ uint32_t s_above;
+    const int r = blockIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int k = a.topk;
+    int32_t *out = a.out_idx + (int64_t)r * k;
+    uint32_t *h1 = (uint32_t *)(a.ws + a.L.hist1) + (int64_t)r * kHist1Slots * kBins1;
+    const int b = clamp_bound(a.row_bound[r], a.max_bound);
+    if (b <= k) {   // every key of the row is selected (uniform exit)
+        for (int j = t; j < k; j += kSelThreads) out[j] = j < b ? j : -1;
+        if (!kHist1 && t < kHist1Slots * kBins1) h1[t] = 0;
+        return;
+    }
+    // ---- the scoring pass's first-digit counts, then the row's keys into
+    // registers (every load issued before any use)
+    uint32_t c1[kHist1Slots] = {};
+    if (!kHist1 && wave == 0) hist1_load(a, r, lane, c1);
+    const int J = (b + kSelThreads - 1) / kSelThreads;   // slices, 2 .. kSmallSlots
+    const float *sc = a.scores + (int64_t)r * a.sstride;
+    // (lanes past the bound re-read the last key: no per-lane branch, and
+    // validity below comes from the one partial slice)
+    float v[kSmallSlots];
+#pragma unroll
+    for (int j = 0; j < kSmallSlots; ++j) {
+        v[j] = 0.0f;
+        if (j < J) v[j] = sc[min(j * kSelThreads + t, b - 1)];
+    }
+    uint32_t key[kSmallSlots];
+#pragma unroll
+    for (int j = 0; j < kSmallSlots; ++j) key[j] = radix_key(v[j]);
+    const int tail = b - (J - 1) * kSelThreads;   // keys in the last slice, 1 .. 1024
+    auto valid = [&](int j) { return (j < J - 1) | (t < tail); };
+
+    // ---- first digit: the k-th largest key's bin and the keys above it
+    uint32_t need = (uint32_t)k;
+    for (int j = t; j < kSmallCopies * kSmallBins; j += kSelThreads) (&shist2[0][0][0])[j] = 0;
+    if (kHist1) {
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kSmallSlots; ++j)
+            if (j < J) small_count_folded(shist2[0][wave & (kSmallCopies - 1)], key[j] >> kDigit1Shift, valid(j), lane);
+        __syncthreads();
+        if (t < kBins1) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int w = 0; w < kSmallCopies; ++w) c += shist2[0][w][t];
+            stot[t] = c;
+        }
+        for (int j = t; j < kSmallCopies * kSmallBins; j += kSelThreads) (&shist2[0][0][0])[j] = 0;
+    } else if (t < kBins1) {
+        stot[t] = hist1_sum(c1);
+    }
     __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-    gather_body(a, 0, r);
+    if (!kHist1 && t < kHist1Slots * kBins1) h1[t] = 0;   // (read above; the workspace is left clean)
+    if (wave == 0) wave_find_bin_regs<1>(stot, need, lane, &s_bin, &s_above);
     __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-    int x0 = 0;   // (opaque, so that finalize compiles as in its own kernel)
-    asm volatile("" : "+s"(r), "+s"(x0));
-    finalize_body(a, x0, r);
+    uint32_t prefix = (uint32_t)s_bin << kDigit1Shift;
+    uint32_t pmask = (uint32_t)(kBins1 - 1) << kDigit1Shift;
+    need -= s_above;
+
+    // ---- the other 26 bits: 9 + 9 + 8 (buffer 0 was cleared above; each
+    // pass clears the other buffer for the next while it sums its own)
+#pragma unroll
+    for (int pass = 0; pass < 3; ++pass) {
+        const int sh = pass == 0 ? 17 : (pass == 1 ? 8 : 0);
+        const uint32_t nb = pass == 2 ? 256u : 512u;
+        uint32_t(*shist)[kSmallBins] = shist2[pass & 1];
+        // A wave whose first slot counts a single digit (heavy ties: then
+        // likely every slot does) folds its adds; other waves add per lane.
+        uint32_t *hw = shist[wave & (kSmallCopies - 1)];
+        const uint32_t d0 = (key[0] >> sh) & (nb - 1);
+        const bool m0 = valid(0) & ((key[0] & pmask) == prefix);
+        const uint64_t act0 = __ballot(m0);
+        bool fold = false;
+        if (act0) {
+            const uint32_t dl = __builtin_amdgcn_readlane(d0, __ffsll((unsigned long long)act0) - 1);
+            fold = __ballot(m0 & (d0 != dl)) == 0;
+        }
+        if (fold) {
+#pragma unroll
+            for (int j = 0; j < kSmallSlots; ++j)
+                if (j < J) small_count(hw, (key[j] >> sh) & (nb - 1), valid(j) & ((key[j] & pmask) == prefix), lane);
+        } else {
+#pragma unroll
+            for (int j = 0; j < kSmallSlots; ++j)
+                if (j < J && (valid(j) & ((key[j] & pmask) == prefix))) atomicAdd(hw + ((key[j] >> sh) & (nb - 1)), 1u);
+        }
+        __syncthreads();
+        if (t < (int)nb) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int w = 0; w < kSmallCopies; ++w) c += shist[w][t];
+            stot[t] = c;
+        }
+        if (pass < 2)
+            for (int j = t; j < kSmallCopies * kSmallBins; j += kSelThreads) (&shist2[(pass + 1) & 1][0][0])[j] = 0;
+        __syncthreads();
+        if (wave == 0) {
+            if (pass < 2) wave_find_bin_regs<kSmallBins / 64>(stot, need, lane, &s_bin, &s_above);
+            else wave_find_bin_regs<4>(stot, need, lane, &s_bin, &s_above);
+        }
+        __syncthreads();
+        prefix |= (uint32_t)s_bin << sh;
+        pmask |= (nb - 1) << sh;
+        need -= s_above;
+    }
+
+    // ---- output in index order (key index = slice * 1024 + wave * 64 + lane)
+    const uint32_t T = prefix;
+#pragma unroll
+    for (int j = 0; j < kSmallSlots; ++j)
+        if (j < J) {
+            const bool ok = valid(j);
+            const uint32_t na = (uint32_t)__popcll(__ballot(ok & (key[j] > T)));
+            const uint32_t ne = (uint32_t)__popcll(__ballot(ok & (key[j] == T)));
+            if (lane == 0) scnt[j * kSmallWaves + wave] = na << 16 | ne;
+        }
+    __syncthreads();
+    if (wave == 0) {   // exclusive prefix of the J * 16 counts (8 per lane); each total is < 2^16
+        const int n = J * kSmallWaves;
+        uint32_t c[8], sum = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            c[e] = 8 * lane + e < n ? scnt[8 * lane + e] : 0u;
+            sum += c[e];
+        }
+        uint32_t run = wave_incl_scan(sum, lane) - sum;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (8 * lane + e < n) scnt[8 * lane + e] = run;
+            run += c[e];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kSmallSlots; ++j)
+        if (j < J) {
+            const bool ok = valid(j);
+            const bool above = ok & (key[j] > T), equal = ok & (key[j] == T);
+            const uint64_t ma = __ballot(above), me = __ballot(equal);
+            const uint32_t base = scnt[j * kSmallWaves + wave];
+            const uint32_t pa = (base >> 16) + lane_prefix(ma), pe = (base & 0xffffu) + lane_prefix(me);
+            const int i = j * kSelThreads + t;
+            if (above) out[pa + min(pe, need)] = i;
+            if (equal & (pe < need)) out[pa + pe] = i;
+        }
 }
 
 __global__ void fill_zero_kernel(uint32_t *p, size_t n) {
@@ -804,11 +1028,12 @@ hipError_t launch_finalize(const SelectArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_select1(const SelectArgs &a, bool with_hist1, hipStream_t st) {
+hipError_t launch_select_small(const SelectArgs &a, bool with_hist1, hipStream_t st) {
+    if (a.max_bound > kSmallMax) return hipErrorInvalidValue;
     if (with_hist1)
-        hipLaunchKernelGGL(select1_kernel<true>, dim3(a.rows), dim3(kSelThreads), 0, st, a);
+        hipLaunchKernelGGL(select_small_kernel<true>, dim3(a.rows), dim3(kSelThreads), 0, st, a);
     else
-        hipLaunchKernelGGL(select1_kernel<false>, dim3(a.rows), dim3(kSelThreads), 0, st, a);
+        hipLaunchKernelGGL(select_small_kernel<false>, dim3(a.rows), dim3(kSelThreads), 0, st, a);
     return hipGetLastError();
 }
 
