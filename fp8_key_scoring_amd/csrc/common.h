@@ -139,6 +139,22 @@ inline WsLayout ws_layout(int rows, int max_bound, bool own_scores, int zero_row
     return L;
 }
 
+// Inclusive prefix sum over the wave's lanes with DPP row shifts (VALU only;
+// a shuffle goes through the LDS crossbar at LDS latency per step): a
+// Hillis-Steele scan inside each row of 16 lanes, then each row adds the
+// totals of the rows before it.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+    const int row = lane >> 4;
+    return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
 // Order-preserving map fp32 -> u32 used as the radix key: larger float ->
 // larger key; -0 and +0 map to the same key; every NaN maps to 0, below -inf.
 __device__ __forceinline__ uint32_t radix_key(float f) {

@@ -74,11 +74,14 @@ __device__ uint32_t merge_scan(uint32_t v, uint32_t *wsum, uint32_t &total) {
 }
 
 // Wave-wide reductions of a 32-bit value (every lane gets the result):
-// shuffles within each 16-lane row, then the rows through permlane swaps.
+// DPP rotations within each 16-lane row (1, 2, 4, 8), then the rows through
+// permlane swaps.
 template <typename F>
 __device__ __forceinline__ uint32_t merge_wave_reduce(uint32_t v, F op) {
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) v = op(v, (uint32_t)__shfl_xor((int)v, o));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xf, 0xf, false));   // row_ror:1
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xf, 0xf, false));   // row_ror:2
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false));   // row_ror:4
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false));   // row_ror:8
     const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
     v = op(a[0], a[1]);
     const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
@@ -181,12 +184,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(int n, int k, cons
             hn[b_hi] = 0u;
             hn[b_hi - 1] = 0u;
             const uint32_t c = c_hi + c_lo;
-            uint32_t incl = c;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t y = (uint32_t)__shfl_up((int)incl, off);
-                if (lane >= off) incl += y;
-            }
+            const uint32_t incl = wave_incl_scan(c, lane);
             if (lane == 63) wsum[wave] = incl;
             __syncthreads();
             uint32_t before = incl - c;

@@ -51,27 +51,33 @@ __device__ __forceinline__ uint32_t lane_prefix(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Executed by one full wave.  h: 64 * per bins in LDS.  Finds the largest bin
-// B with sum_{b >= B} h[b] >= need (need >= 1) and the count strictly above
-// B.  Results land in *outB / *outAbove (LDS), written by one lane.
-__device__ void wave_find_bin(const uint32_t *h, int per, uint32_t need, int lane,
-                              int *outB, uint32_t *outAbove) {
-    uint32_t mine = 0;
-    for (int j = 0; j < per; ++j) mine += h[lane * per + j];
-    uint32_t incl = mine;   // sum over lanes >= lane
-    for (int off = 1; off < 64; off <<= 1) {
-        uint32_t v = __shfl_down(incl, off);
-        if (lane + off < 64) incl += v;
+// Executed by one full wave.  h: 64 * PER bins in LDS.  Finds the largest
+// bin B with sum_{b >= B} h[b] >= need (need >= 1) and the count strictly
+// above B.  Results land in *outB / *outAbove (LDS), written by one lane.
+// A lane's PER counts stay in registers for the final walk.
+template <int PER>
+__device__ __forceinline__ void wave_find_bin(const uint32_t *h, uint32_t need, int lane, int *outB,
+                                              uint32_t *outAbove) {
+    uint32_t c[PER], mine = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        c[j] = h[lane * PER + j];
+        mine += c[j];
     }
-    const uint32_t excl = incl - mine;
-    const uint64_t m = __ballot(excl < need && need <= incl);
-    const int L = m ? (__ffsll((unsigned long long)m) - 1) : -1;
-    if (lane == L) {
-        uint32_t cum = excl;
-        for (int j = per - 1; j >= 0; --j) {
-            const uint32_t c = h[L * per + j];
-            if (cum + c >= need) { *outB = L * per + j; *outAbove = cum; break; }
-            cum += c;
+    const uint32_t incl = wave_incl_scan(mine, lane);
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    const uint32_t above_lane = total - incl;   // lanes after this one (higher bins)
+    const uint64_t m = __ballot((above_lane < need) & (need <= above_lane + mine));
+    if (m && lane == __ffsll((unsigned long long)m) - 1) {
+        uint32_t cum = above_lane;
+#pragma unroll
+        for (int j = PER - 1; j >= 0; --j) {
+            if (cum + c[j] >= need) {
+                *outB = lane * PER + j;
+                *outAbove = cum;
+                break;
+            }
+            cum += c[j];
         }
     }
 }
@@ -80,11 +86,7 @@ __device__ void wave_find_bin(const uint32_t *h, int per, uint32_t need, int lan
 // index order); *total gets the sum.
 __device__ void wave_scan128(uint32_t *c, uint32_t *total, int lane) {
     const uint32_t c0 = c[2 * lane], c1 = c[2 * lane + 1];
-    uint32_t incl = c0 + c1;
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t v = __shfl_up(incl, off);
-        if (lane >= off) incl += v;
-    }
+    const uint32_t incl = wave_incl_scan(c0 + c1, lane);
     const uint32_t excl = incl - c0 - c1;
     c[2 * lane] = excl;
     c[2 * lane + 1] = excl + c0;
@@ -213,7 +215,7 @@ __device__ __forceinline__ void refine_body(const SelectArgs &a, int x, int r) {
     for (int i = t; i < 4 * kBins2; i += kSelThreads) (&h2[0][0])[i] = 0;
     if (t == 0) { sb1 = 0; sabove1 = 0; }
     __syncthreads();
-    if (t < 64) wave_find_bin(h1, 1, k, lane, &sb1, &sabove1);
+    if (t < 64) wave_find_bin<1>(h1, k, lane, &sb1, &sabove1);
     __syncthreads();
     const uint32_t b1 = (uint32_t)sb1;
     if (x == 0 && t == 0) {   // the split's first half, for gather
@@ -290,7 +292,7 @@ __device__ __forceinline__ void gather_body(const SelectArgs &a, int x, int r) {
     }
     if (t == 0) { sb2 = 0; sabove2 = 0; }
     __syncthreads();
-    if (t < 64) wave_find_bin(h2, kBins2 / 64, (uint32_t)k - above1, lane, &sb2, &sabove2);
+    if (t < 64) wave_find_bin<kBins2 / 64>(h2, (uint32_t)k - above1, lane, &sb2, &sabove2);
     __syncthreads();
     const uint32_t b2 = (uint32_t)sb2;
     const uint32_t T14 = (b1 << kDigit2Bits) | b2;
@@ -567,11 +569,8 @@ __device__ __forceinline__ void finalize_body(const SelectArgs &a, int xw, int r
             // with counters left dirty by a misused workspace) is never read
             // past its end: the row takes the fallback instead
             const uint64_t big = __ballot(cc > (uint32_t)kCandSlice || c > (uint32_t)kSliceCap);
-            uint32_t incl = c, cincl = cc, rincl = rm;
-            for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t v = __shfl_up(incl, o), w = __shfl_up(cincl, o), z = __shfl_up(rincl, o);
-                if (lane >= o) { incl += v; cincl += w; rincl += z; }
-            }
+            const uint32_t incl = wave_incl_scan(c, lane), cincl = wave_incl_scan(cc, lane),
+                           rincl = wave_incl_scan(rm, lane);
             offe[lane] = incl - c;
             roff[lane] = rincl - rm;
             if (lane == 63) {
@@ -585,7 +584,7 @@ __device__ __forceinline__ void finalize_body(const SelectArgs &a, int xw, int r
         __syncthreads();
         // the third-digit bin of the k-th key and the keys in it: the same
         // decision in every workgroup of the row
-        if (t < 64) wave_find_bin(h3, kBins3 / 64, (uint32_t)need, lane, &sB, &sAbove);
+        if (t < 64) wave_find_bin<kBins3 / 64>(h3, (uint32_t)need, lane, &sB, &sAbove);
         __syncthreads();
         const int N = (int)offe[kSelMaxWgs];
         overflow = ovf != 0u || h3[sB] > (uint32_t)kTieCap;
@@ -701,7 +700,7 @@ __device__ __forceinline__ void finalize_body(const SelectArgs &a, int xw, int r
                     if (h10[i]) __hip_atomic_fetch_add(&g10[i], h10[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             if (alone) {
-                if (t < 64) wave_find_bin(h10, kFbBins / 64, need2, lane, &sB10, &sAbove10);
+                if (t < 64) wave_find_bin<kFbBins / 64>(h10, need2, lane, &sB10, &sAbove10);
                 __syncthreads();
                 fallback_output(a.scores + (int64_t)r * a.sstride, b, (T22 << kFbBits) | (uint32_t)sB10,
                                 need2 - sAbove10, out_row, k, wsum2);
@@ -733,7 +732,7 @@ __device__ __forceinline__ void finalize_body(const SelectArgs &a, int xw, int r
             }
         }
         __syncthreads();
-        if (t < 64) wave_find_bin(h10, kFbBins / 64, need2, lane, &sB10, &sAbove10);
+        if (t < 64) wave_find_bin<kFbBins / 64>(h10, need2, lane, &sB10, &sAbove10);
         __syncthreads();
         fallback_output(a.scores + (int64_t)r * a.sstride, b, (T22 << kFbBits) | (uint32_t)sB10,
                         need2 - sAbove10, out_row, k, wsum2);
@@ -773,51 +772,6 @@ constexpr int kSmallSlots = kSmallMax / kSelThreads;   // keys per thread
 constexpr int kSmallBins = 512;
 constexpr int kSmallCopies = 8;   // histogram copies (wave % 8)
 static_assert(kSmallSlots * kSmallWaves <= 64 * 8, "the output scan covers 8 counts per lane");
-
-// Inclusive prefix sum over the wave's lanes with DPP row shifts (VALU only;
-// a shuffle goes through the LDS crossbar at LDS latency per step): a
-// Hillis-Steele scan inside each row of 16 lanes, then each row adds the
-// totals of the rows before it.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane) {
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
-    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
-    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
-    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
-    const int row = lane >> 4;
-    return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
-}
-
-// wave_find_bin for the short-row path (one full wave; h: 64 * PER bins in
-// LDS, PER <= 8): the lane sums and the final walk stay in registers.
-template <int PER>
-__device__ __forceinline__ void wave_find_bin_regs(const uint32_t *h, uint32_t need, int lane, int *outB,
-                                                   uint32_t *outAbove) {
-    uint32_t c[PER], mine = 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        c[j] = h[lane * PER + j];
-        mine += c[j];
-    }
-    const uint32_t incl = wave_incl_scan(mine, lane);
-    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-    const uint32_t above_lane = total - incl;   // lanes after this one (higher bins)
-    const uint64_t m = __ballot((above_lane < need) & (need <= above_lane + mine));
-    if (m && lane == __ffsll((unsigned long long)m) - 1) {
-        uint32_t cum = above_lane;
-#pragma unroll
-        for (int j = PER - 1; j >= 0; --j) {
-            if (cum + c[j] >= need) {
-                *outB = lane * PER + j;
-                *outAbove = cum;
-                break;
-            }
-            cum += c[j];
-        }
-    }
-}
 
 // Digit counts of up to four distinct digits folded per wave (the first
 // digit: a row's keys share few of them, and same-address LDS atomics of one
@@ -909,7 +863,7 @@ __global__ __launch_bounds__(kSelThreads) void select_small_kernel(SelectArgs a)
     }
     __syncthreads();
     if (!kHist1 && t < kHist1Slots * kBins1) h1[t] = 0;   // (read above; the workspace is left clean)
-    if (wave == 0) wave_find_bin_regs<1>(stot, need, lane, &s_bin, &s_above);
+    if (wave == 0) wave_find_bin<1>(stot, need, lane, &s_bin, &s_above);
     __syncthreads();
     uint32_t prefix = (uint32_t)s_bin << kDigit1Shift;
     uint32_t pmask = (uint32_t)(kBins1 - 1) << kDigit1Shift;
@@ -953,8 +907,8 @@ __global__ __launch_bounds__(kSelThreads) void select_small_kernel(SelectArgs a)
             for (int j = t; j < kSmallCopies * kSmallBins; j += kSelThreads) (&shist2[(pass + 1) & 1][0][0])[j] = 0;
         __syncthreads();
         if (wave == 0) {
-            if (pass < 2) wave_find_bin_regs<kSmallBins / 64>(stot, need, lane, &s_bin, &s_above);
-            else wave_find_bin_regs<4>(stot, need, lane, &s_bin, &s_above);
+            if (pass < 2) wave_find_bin<kSmallBins / 64>(stot, need, lane, &s_bin, &s_above);
+            else wave_find_bin<4>(stot, need, lane, &s_bin, &s_above);
         }
         __syncthreads();
         prefix |= (uint32_t)s_bin << sh;
