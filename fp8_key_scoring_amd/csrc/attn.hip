@@ -366,13 +366,9 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
     if (t < 64) {   // wave 0: lane x holds split x (nsplit <= 32)
         const float m = t < a.nsplit ? ml[t * 2 * kAH + h] : -INFINITY;
         const float l = t < a.nsplit ? ml[t * 2 * kAH + kAH + h] : 0.0f;
-        float M = m;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+        const float M = wave_max_f32(m);
         const float w = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-        float L = w * l;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o);
+        const float L = wave_sum_f32(w * l);
         if (t < kAttnMaxSplit) wsc[t] = w;
         if (t == 0) {
             inv_l = L > 0.0f ? 1.0f / L : 0.0f;

@@ -155,6 +155,31 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane) {
     return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
 }
 
+// Wave-wide maximum and sum of a float, every lane getting the result: DPP
+// rotations within each 16-lane row (1, 2, 4, 8), then the four rows through
+// the two permlane swaps (each lane combines its value with the one 32, then
+// 16, lanes away).
+__device__ __forceinline__ float wave_max_f32(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false)));
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+    v = fmaxf(__int_as_float(a[0]), __int_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return fmaxf(__int_as_float(b[0]), __int_as_float(b[1]));
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+    v = __int_as_float(a[0]) + __int_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return __int_as_float(b[0]) + __int_as_float(b[1]);
+}
+
 // Order-preserving map fp32 -> u32 used as the radix key: larger float ->
 // larger key; -0 and +0 map to the same key; every NaN maps to 0, below -inf.
 __device__ __forceinline__ uint32_t radix_key(float f) {

@@ -40,8 +40,7 @@ __global__ __launch_bounds__(64) void write_keys_kernel(const uint16_t *k_new, u
 
     const uint32_t two = ((const uint32_t *)(k_new + (int64_t)r * kDim))[lane];   // elements 2l, 2l+1
     const float x0 = __uint_as_float(two << 16), x1 = __uint_as_float(two & 0xffff0000u);
-    float amax = fmaxf(fabsf(x0), fabsf(x1));
-    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const float amax = wave_max_f32(fmaxf(fabsf(x0), fabsf(x1)));
     const bool zero = amax == 0.0f;
     const float scale = zero ? 1.0f : __fdiv_rn(amax, 448.0f);
     const int packed = __builtin_amdgcn_cvt_pk_fp8_f32(__fdiv_rn(x0, scale), __fdiv_rn(x1, scale), 0, false);
