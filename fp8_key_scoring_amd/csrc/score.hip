@@ -46,10 +46,12 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // 16-key groups loaded ahead per wave (a multiple of 4).  A group feeds 16
-// MFMAs per row, so with 3-4 rows four groups ahead cover as much time as
-// eight with 1-2 rows, in half the registers.
+// MFMAs per row; eight groups ahead pay only for one row over a long context
+// (1 row x 524,288 keys: 19.5 against 20.2 us with four); with two rows four
+// are faster (2 rows x 524,288 keys: 21.6 against 23.1 us with eight: the
+// start-up burst of every wave's ring is half as long).
 template <int R>
-constexpr int ring_depth() { return R >= 3 ? 4 : 8; }
+constexpr int ring_depth() { return R >= 2 ? 4 : 8; }
 
 __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
     bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
