@@ -49,7 +49,10 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // MFMAs per row; eight groups ahead pay only for one row over a long context
 // (1 row x 524,288 keys: 19.5 against 20.2 us with four); with two rows four
 // are faster (2 rows x 524,288 keys: 21.6 against 23.1 us with eight: the
-// start-up burst of every wave's ring is half as long).
+// start-up burst of every wave's ring is half as long).  The loop runs whole
+// rings, so a wave with fewer groups than its ring computes (and discards)
+// the difference: one row's waves with fewer than 16 groups take four.
+constexpr int kDeepRingGroups = 16;
 template <int R>
 constexpr int ring_depth() { return R >= 2 ? 4 : 8; }
 
@@ -172,11 +175,10 @@ struct WaveJob {
 // row) the conversion of the next group and the refill of its ring slot are
 // independent, and the scheduler interleaves them: one MFMA, then a few VALU
 // ops.  A group's keys are converted once and used by all R rows.
-template <int R, bool kHist>
+template <int R, bool kHist, int kRing = ring_depth<R>()>
 __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j, unsigned char *lds_q,
                                            bf16_t *t1_lds, uint32_t *lds_cnt, int q_slot, bool staged,
                                            float w_blk) {
-    constexpr int kRing = ring_depth<R>();
     const int lane = j.lane;
     const int kig = lane & 15;      // key of the group this lane loads / scores
     const int lrow = lane >> 4;     // lane row: 32-byte quarter of the key, 4-head slice of D
@@ -583,7 +585,10 @@ void score_kernel(ScoreArgs a) {
         case 4: score_rows<4, kHist>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, w_blk); break;
         case 3: score_rows<3, kHist>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, w_blk); break;
         case 2: score_rows<2, kHist>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, w_blk); break;
-        default: score_rows<1, kHist>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, w_blk); break;
+        default:
+            if (job.n_my >= kDeepRingGroups) score_rows<1, kHist>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, w_blk);
+            else score_rows<1, kHist, 4>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, w_blk);
+            break;
         }
 
         // ---- add the chunk's first-digit counts to the row totals: wave r
