@@ -471,12 +471,18 @@ void score_kernel(ScoreArgs a) {
     // known to lie in the block).  Loads complete in order, so the planning
     // loads must be issued first for the planning to wait on them alone.
     __builtin_amdgcn_sched_barrier(0);
+    // (piece c of every thread belongs to block row c / 4: rows past the last
+    // are not loaded, so a block of one or two rows reads only their q and the
+    // page-table load behind it returns sooner)
+    static_assert(kScoreThreads * 4 == kHeads * kDim / 8, "four pieces per thread per row");
+    const int rows_blk = min(a.rows - yb, kGroupRows);
     u32x4_t qt_blk[kBlockPieces];
 #pragma unroll
     for (int c = 0; c < kBlockPieces; ++c) {
         const int ci = threadIdx.x + c * kScoreThreads;   // piece index: row, head, piece
-        const int row = min(yb + (ci >> 10), a.rows - 1);   // rows past the end: never used
-        qt_blk[c] = *(gptr<u32x4_t>)(a.q + ((int64_t)row * kHeads + ((ci >> 4) & 63)) * kDim + 8 * (ci & 15));
+        if ((c >> 2) < rows_blk)
+            qt_blk[c] = *(gptr<u32x4_t>)(a.q + ((int64_t)(yb + (c >> 2)) * kHeads + ((ci >> 4) & 63)) * kDim +
+                                         8 * (ci & 15));
     }
     const float w_blk = a.w[(int64_t)min(yb + wave, a.rows - 1) * kHeads + lane];
     __builtin_amdgcn_sched_barrier(0);
@@ -540,7 +546,7 @@ void score_kernel(ScoreArgs a) {
 #pragma unroll
         for (int c = 0; c < kBlockPieces; ++c) {
             const int ci = threadIdx.x + c * kScoreThreads;
-            *(u32x4_t *)(lds_q + q_lds_off(ci >> 10, (ci >> 4) & 63, ci & 15)) = qt_blk[c];
+            if ((c >> 2) < rows_blk) *(u32x4_t *)(lds_q + q_lds_off(ci >> 10, (ci >> 4) & 63, ci & 15)) = qt_blk[c];
         }
         lds_barrier();   // (the page ids may still be in flight)
     }
