@@ -9,7 +9,8 @@ chain that longer launches take.
     chain runs) give the same selection;
   * fused launches (the first digit from the scoring pass, cleared by the
     selection): all-equal keys, many requests of mixed lengths; the
-    workspace's zero block is zero after every launch.
+    workspace's zero block is zero after every launch, also when the launch
+    runs as its two stages (indexer_launch_score, indexer_launch_select).
 """
 import numpy as np
 import pytest
@@ -93,3 +94,26 @@ def test_short_launch_leaves_the_workspace_clean():
         assert np.array_equal(out, ref)
     _, want = run_launch(p)
     assert np.array_equal(ref, want)
+
+
+def test_short_launch_in_two_stages():
+    # indexer_launch_score then indexer_launch_select: the short-row selection
+    # takes the first-digit counts the scoring stage left and clears them
+    p = syn.build_problem("short_stages", 9, [SHORT, 5000], syn.verify_rows(0, SHORT) + syn.verify_rows(1, 5000),
+                          dup_frac=0.01)
+    say("[gpu] short rows: launch vs its two stages")
+    s1, o1 = run_launch(p)
+    d = syn.device_arrays(p, "cuda:0")
+    mb = p.max_bound
+    prob = fk._problem_from(d["q"], d["k_e4m3"], d["page_table"], mb, p.topk, 0)
+    for own in (False, True):
+        ws = fk.new_workspace(prob, own, "cuda:0")
+        for rep in range(2):
+            sc = None if own else torch.full((p.rows, mb), float("nan"), dtype=torch.float32, device="cuda:0")
+            fk.indexer_launch_score(**d, max_bound=mb, topk=p.topk, scores=sc, workspace=ws)
+            o2 = fk.indexer_launch_select(d["row_bound"], max_bound=mb, topk=p.topk, scores=sc, workspace=ws)
+            torch.cuda.synchronize()
+            if sc is not None:
+                assert np.array_equal(s1.view(np.uint32), sc.cpu().numpy().view(np.uint32))
+            assert np.array_equal(o1, o2.cpu().numpy()), (own, rep)
+            assert not ws[:_zero_block_bytes(p.rows)].any(), (own, rep)
