@@ -615,10 +615,239 @@ void score_kernel(ScoreArgs a) {
     }
 }
 
+// ===========================================================================
+// One-row launches (a single query row: decode with no speculative rows).
+// One row's q is 64 registers, so the wave fits in half the register file
+// and each SIMD runs two waves: 8 waves per workgroup, wave w taking page w
+// of every block of 8 pages of the chunk.  The loop is straight-line: while
+// one wave converts keys and runs its epilogue, the other wave of the SIMD
+// issues MFMAs and key loads.  The row needs no planning of row groups: its
+// page-table row and bound are two scalar loads.
+constexpr int kRowThreads = 512;
+constexpr int kRowWaves = kRowThreads / 64;
+constexpr int kRowRingPages = 1;                 // pages of keys in flight per wave
+constexpr int kRowRing = 4 * kRowRingPages;      // 16-key groups in flight per wave
+constexpr int kLdsQRow = kHeads * kDim * 2;      // 16 KB: q of the row, then the counters
+constexpr int kHistLdsRow = kRowWaves * kBins1 * kCntCopies;
+static_assert(kHistLdsRow * 4 <= kLdsQRow, "the counters reuse the q region");
+
+template <bool kHist>
+__global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void score_row_kernel(ScoreArgs a) {
+    extern __shared__ __align__(16) unsigned char lds_dyn[];
+    unsigned char *lds_q = lds_dyn;
+    bf16_t *t1_lds = (bf16_t *)(lds_dyn + kLdsQRow);
+    uint32_t *lds_cnt = (uint32_t *)lds_dyn;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kig = lane & 15;
+    const int lrow = lane >> 4;
+    const uint32_t koff = (uint32_t)(kig * kDim + lrow * 32);
+
+    // page-table row and bound first (the page ids wait on them), then q
+    // (two 16-byte pieces per thread) and the weights, which wait on nothing
+    const int pr = a.row_pt[0];
+    int bnd = a.row_bound[0];
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int kPieces = kHeads * kDim / 8 / kRowThreads;
+    static_assert(kPieces * kRowThreads * 8 == kHeads * kDim, "whole pieces per thread");
+    u32x4_t qt[kPieces];
+#pragma unroll
+    for (int c = 0; c < kPieces; ++c) {
+        const int ci = tid + c * kRowThreads;   // piece index: head ci / 16, piece ci % 16
+        qt[c] = *(gptr<u32x4_t>)(a.q + (ci >> 4) * kDim + 8 * (ci & 15));
+    }
+    // weights (halved) of the D rows a lane holds: heads 16*hb + 4*(lane/16) + jj
+    f32x4_t wv[4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) wv[hb] = *(gptr<f32x4_t>)(a.w + 16 * hb + 4 * lrow) * 0.5f;
+    const float w_lane = a.w[lane];
+    __builtin_amdgcn_sched_barrier(0);
+    bnd = bnd < 0 ? 0 : (bnd > a.max_bound ? a.max_bound : bnd);
+    const int c0 = blockIdx.x * a.chunk;
+    if (c0 >= bnd) return;   // (uniform over the workgroup)
+    const int c1 = min(c0 + a.chunk, bnd);
+    const int gc0 = c0 / kKeysPerMfma;
+    int vpage;
+    {
+        const bool pt_ok = pr >= 0 && pr < a.pt_rows;
+        const int npg = (c1 - c0 + kPage - 1) / kPage;
+        const int32_t *pt = a.page_table + (int64_t)(pt_ok ? pr : 0) * a.pt_stride + c0 / kPage;
+        const int v = (pt_ok && lane < npg) ? pt[lane] : -1;
+        vpage = (v >= 0 && v < a.num_pages) ? v : -1;
+    }
+    // the wave's groups: its i-th is gbase + 32 * (i / 4) + i % 4, groups
+    // below the chunk's end: 4 per whole block of 32, up to 4 of the last
+    const int gbase = gc0 + 4 * wave;
+    const int rem = (c1 + kKeysPerMfma - 1) / kKeysPerMfma - gbase;
+    const int n_my = rem > 0 ? 4 * (rem >> 5) + min(rem & 31, 4) : 0;
+    auto group = [&](int i) { return gbase + 32 * (i >> 2) + (i & 3); };
+    // loads past the wave's last group re-read that group (no branch)
+    auto load_group = [&](int i, KeyGroup &kg) {
+        const int ic = max(min(i, n_my - 1), 0);
+        const int g = group(ic);
+        const int page = __builtin_amdgcn_readlane(vpage, (g - gc0) >> 2);
+        kg.ok = page >= 0;
+        const int64_t key0 = (int64_t)(kg.ok ? page : 0) * kPage + (g & 3) * kKeysPerMfma;
+        gptr<uint8_t> kbase = scalar_ptr(a.k8 + key0 * kDim);
+        gptr<float> sbase = scalar_ptr(a.kscale + key0);
+        kg.lo = *(gptr<u32x4_t>)(kbase + koff);
+        kg.hi = *(gptr<u32x4_t>)(kbase + koff + 16);
+        kg.scale = sbase[kig];
+    };
+    KeyGroup kb[kRowRing];
+#pragma unroll
+    for (int p = 0; p < kRowRing; ++p) load_group(p, kb[p]);
+
+    // q to LDS, then back in MFMA A-operand order into AGPRs
+#pragma unroll
+    for (int c = 0; c < kPieces; ++c) {
+        const int ci = tid + c * kRowThreads;
+        *(u32x4_t *)(lds_q + q_lds_off(0, ci >> 4, ci & 15)) = qt[c];
+    }
+    lds_barrier();
+    bf16x8_t qa[4][4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qa[hb][ks] = *(const bf16x8_t *)(lds_q + q_lds_off(0, 16 * hb + kig, 4 * lrow + ks));
+    // the linear term's A operand (as in score_rows, with one row): A row 4p
+    // holds part p (hi, mid, lo bf16) of u = (1/2) sum_h w_h q_h, computed
+    // by the last wave, lane l dims 2l and 2l+1
+    if (wave == kRowWaves - 1) {
+        float u0 = 0.0f, u1 = 0.0f;
+#pragma unroll
+        for (int h0 = 0; h0 < kHeads; h0 += 8) {
+            uint32_t qw[8];
+#pragma unroll
+            for (int h = 0; h < 8; ++h) qw[h] = *(const uint32_t *)(lds_q + q_lds_off(0, h0 + h, lane >> 2) + (lane & 3) * 4);
+#pragma unroll
+            for (int h = 0; h < 8; ++h) {
+                const float wh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), h0 + h));
+                u0 = fmaf(wh, __uint_as_float(qw[h] << 16), u0);
+                u1 = fmaf(wh, __uint_as_float(qw[h] & 0xffff0000u), u1);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float u = (e ? u1 : u0) * 0.5f;
+            const int d = 2 * lane + e;
+            const bf16_t hi = (bf16_t)u;
+            const float r1 = u - (float)hi;
+            const bf16_t mid = (bf16_t)r1;
+            const bf16_t lo = (bf16_t)(r1 - (float)mid);
+            const int ks = (d & 31) >> 3, lr = d >> 5;
+            t1_lds[(ks * 64 + 0 + 16 * lr) * 8 + (d & 7)] = hi;
+            t1_lds[(ks * 64 + 4 + 16 * lr) * 8 + (d & 7)] = mid;
+            t1_lds[(ks * 64 + 8 + 16 * lr) * 8 + (d & 7)] = lo;
+        }
+    }
+    lds_barrier();   // q in LDS is read and u is written
+    bf16x8_t t1a[4];
+    {
+        const bool t1_row = (kig >> 2) < 3 && (kig & 3) == 0;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8_t v = *(const bf16x8_t *)(t1_lds + (ks * 64 + lane) * 8);
+            t1a[ks] = t1_row ? v : bf16x8_t{};
+        }
+    }
+    if (kHist) {   // the q region becomes the counters
+        u32x4_t *c4 = (u32x4_t *)lds_cnt;
+        const uint32_t z = (uint32_t)tid >> 16;   // 0, built here rather than kept live
+        for (int i = tid; i < kHistLdsRow / 4; i += kRowThreads) c4[i] = u32x4_t{z, z, z, z};
+        lds_barrier();
+    }
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+a"(qa[hb][ks]));
+
+    const int nrec = min(bnd - c0, a.chunk) * 4;   // the row's keys [c0, bound) of the chunk, in bytes
+    const __amdgpu_buffer_rsrc_t out_row = __builtin_amdgcn_make_buffer_rsrc((void *)(a.scores + c0), 0, nrec, kBufferFlags);
+    float P[4];
+    float sv = 0.0f;   // lane l: scale of key l of the page being scored
+    // one pass over the ring per kRowRingPages pages; the last pass stops
+    // after the wave's last page
+    for (int i0 = 0; i0 < n_my; i0 += kRowRing) {
+#pragma unroll
+        for (int pg = 0; pg < kRowRingPages; ++pg) {
+            const int ip = i0 + 4 * pg;   // the page's first group (wave's index)
+            if (pg > 0 && ip >= n_my) break;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                KeyGroup &kg = kb[4 * pg + p];
+                bf16x8_t kv[4];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const u32x4_t &src = ks < 2 ? kg.lo : kg.hi;
+                    kv[ks] = e4m3x8_to_bf16(src[(ks & 1) * 2], src[(ks & 1) * 2 + 1]);
+                }
+                sv = lrow == p ? (kg.ok ? kg.scale : __builtin_nanf("")) : sv;
+                load_group(ip + p + kRowRing, kg);
+                f32x4_t t1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t1a[ks], kv[ks], t1, 0, 0, 0);
+                f32x4_t acc[4];
+#pragma unroll
+                for (int hb = 0; hb < 4; ++hb) acc[hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                    for (int hb = 0; hb < 4; ++hb)
+                        acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[hb][ks], kv[ks], acc[hb], 0, 0, 0);
+                // sum_h w_h max(d_h, 0) = u . k + sum_h (w_h / 2) |d_h| (the
+                // epilogue of score_rows); lane l's 16 heads of key l % 16
+                float part = t1[0];
+#pragma unroll
+                for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) part = fmaf(wv[hb][jj], fabsf(acc[hb][jj]), part);
+                P[p] = part;
+                // groups stay in order: the other wave of the SIMD fills the
+                // gaps (letting the compiler interleave groups cost ~0.5 us
+                // per launch)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // the page's scores: lane l holds key l of the page; keys past the
+            // bound or the wave's groups fall outside the buffer and are dropped
+            const float out = reduce4(P[0], P[1], P[2], P[3]) * sv;
+            const int s = group(ip) * kKeysPerMfma + lane;
+            const bool in_job = ip + lrow < n_my;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), out_row, in_job ? (s - c0) * 4 : nrec, 0, 0);
+            if (kHist) {
+                const uint32_t d = radix_key(out) >> kDigit1Shift;
+                atomicAdd(lds_cnt + (wave * kBins1 + d) * kCntCopies + lane % kCntCopies, (in_job && s < bnd) ? 1u : 0u);
+            }
+        }
+    }
+    if (kHist) {   // the row's counts (lane = digit) summed over the waves by the first wave
+        lds_barrier();
+        if (wave == 0) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int w = 0; w < kRowWaves; ++w) {
+                const u32x4_t v4 = *(const u32x4_t *)(lds_cnt + (w * kBins1 + lane) * kCntCopies);
+                c += v4[0] + v4[1] + v4[2] + v4[3];
+            }
+            if (c) atomicAdd(a.hist1 + (blockIdx.x % kHist1Slots) * kBins1 + lane, c);
+        }
+    }
+}
+
 hipError_t launch_score(const ScoreArgs &a, hipStream_t st) {
     if (a.max_bound <= 0) return hipSuccess;
     const int nchunks = (a.max_bound + a.chunk - 1) / a.chunk;
     dim3 grid(nchunks, (a.rows + kGroupRows - 1) / kGroupRows);
+    if (a.rows == 1) {
+        const size_t lds = (size_t)kLdsQRow + kLdsT1;
+        if (a.hist1)
+            hipLaunchKernelGGL(score_row_kernel<true>, grid, dim3(kRowThreads), lds, st, a);
+        else
+            hipLaunchKernelGGL(score_row_kernel<false>, grid, dim3(kRowThreads), lds, st, a);
+        return hipGetLastError();
+    }
     const size_t lds = (size_t)kLdsQ + kLdsT1;
     if (a.hist1)
         hipLaunchKernelGGL(score_kernel<true>, grid, dim3(kScoreThreads), lds, st, a);
