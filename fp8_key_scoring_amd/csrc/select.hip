@@ -761,8 +761,11 @@ __global__ __launch_bounds__(kSelThreads) void finalize_kernel(SelectArgs a) {
 // counts in the workspace (the kernel clears them) or counted here; then bits
 // 25..17, 16..8 and 7..0 (512, 512 and 256 bins) in eight LDS histogram
 // copies (wave % 8), double-buffered so that one is cleared while the other
-// counts.  LDS adds are one per counted key and lane; a wave whose keys share
-// one digit (heavy ties) folds them into one add.  Wave scans use DPP row
+// counts.  Once at most 64 keys share the 15-bit prefix (after the first of
+// those passes, for all but heavily tied rows) they are ranked directly and
+// the last two passes are skipped.  LDS adds are one per counted key and
+// lane; a wave whose keys share one digit (heavy ties) folds them into one
+// add.  Wave scans use DPP row
 // shifts (a shuffle goes through the LDS crossbar at LDS latency per step).
 // Output: per 1024-key slice, each wave's counts of keys above and equal to T
 // (ballots), one scan of those counts in index order, then every lane writes
@@ -771,6 +774,8 @@ constexpr int kSmallWaves = kSelThreads / 64;
 constexpr int kSmallSlots = kSmallMax / kSelThreads;   // keys per thread
 constexpr int kSmallBins = 512;
 constexpr int kSmallCopies = 8;   // histogram copies (wave % 8)
+constexpr int kSmallRank = 64;    // a bin of at most this many keys is ranked directly
+static_assert(kSmallRank % kSmallWaves == 0 && kSmallRank <= 64, "direct rank: whole comparisons per thread, one candidate per lane");
 static_assert(kSmallSlots * kSmallWaves <= 64 * 8, "the output scan covers 8 counts per lane");
 
 // Digit counts of up to four distinct digits folded per wave (the first
@@ -811,6 +816,10 @@ __global__ __launch_bounds__(kSelThreads) void select_small_kernel(SelectArgs a)
     __shared__ uint32_t scnt[kSmallSlots * kSmallWaves];   // [slice][wave]: above << 16 | equal, then their prefix
     __shared__ int s_bin;
     __shared__ uint32_t s_above;
+    __shared__ uint32_t s_rk[kSmallRank];   // the keys of a small bin and their indices
+    __shared__ int s_ri[kSmallRank];
+    __shared__ uint32_t s_rank[kSmallRank];
+    __shared__ uint32_t s_nr, s_T, s_need;
     const int r = blockIdx.x;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int k = a.topk;
@@ -844,6 +853,8 @@ __global__ __launch_bounds__(kSelThreads) void select_small_kernel(SelectArgs a)
 
     // ---- first digit: the k-th largest key's bin and the keys above it
     uint32_t need = (uint32_t)k;
+    if (t == 0) s_nr = 0;
+    if (t < kSmallRank) s_rank[t] = 0;
     for (int j = t; j < kSmallCopies * kSmallBins; j += kSelThreads) (&shist2[0][0][0])[j] = 0;
     if (kHist1) {
         __syncthreads();
@@ -914,6 +925,52 @@ __global__ __launch_bounds__(kSelThreads) void select_small_kernel(SelectArgs a)
         prefix |= (uint32_t)s_bin << sh;
         pmask |= (nb - 1) << sh;
         need -= s_above;
+        if (pass == 0 && stot[s_bin] <= (uint32_t)kSmallRank) {
+            // few keys share the prefix (the usual case after 15 bits): they
+            // are ranked directly, (key desc, index asc), and the need-th is
+            // T; the digit passes that remain are skipped.  Thread t compares
+            // candidate t % 64 with candidates 4 (t / 64) .. 4 (t / 64) + 3.
+            const uint32_t nbin = stot[s_bin];
+#pragma unroll
+            for (int j = 0; j < kSmallSlots; ++j)
+                if (j < J && (valid(j) & ((key[j] & pmask) == prefix))) {
+                    const uint32_t slot = atomicAdd(&s_nr, 1u);
+                    if (slot < (uint32_t)kSmallRank) {
+                        s_rk[slot] = key[j];
+                        s_ri[slot] = j * kSelThreads + t;
+                    }
+                }
+            __syncthreads();
+            const uint32_t ci = (uint32_t)lane;
+            if (ci < nbin) {
+                const uint32_t kl = s_rk[ci];
+                const int il = s_ri[ci];
+                uint32_t c = 0;
+#pragma unroll
+                for (int q = 0; q < kSmallRank / kSmallWaves; ++q) {
+                    const uint32_t f = (uint32_t)(wave * (kSmallRank / kSmallWaves) + q);
+                    if (f < nbin) {
+                        const uint32_t kf = s_rk[f];
+                        const int jf = s_ri[f];
+                        c += (kf > kl) || (kf == kl && jf < il);
+                    }
+                }
+                if (c) atomicAdd(&s_rank[ci], c);
+            }
+            __syncthreads();
+            if (wave == 0) {
+                const bool mine = (uint32_t)lane < nbin;
+                const uint32_t kl = mine ? s_rk[lane] : 0u;
+                const uint64_t at = __ballot(mine && s_rank[lane] == need - 1);   // exactly one lane
+                const uint32_t T = (uint32_t)__builtin_amdgcn_readlane((int)kl, __ffsll((unsigned long long)at) - 1);
+                const uint32_t above = (uint32_t)__popcll(__ballot(mine && kl > T));
+                if (lane == 0) { s_T = T; s_need = need - above; }
+            }
+            __syncthreads();
+            prefix = s_T;
+            need = s_need;
+            break;
+        }
     }
 
     // ---- output in index order (key index = slice * 1024 + wave * 64 + lane)
