@@ -526,7 +526,7 @@ __device__ __forceinline__ void finalize_body(const SelectArgs &a, int xw, int r
     constexpr int kPre = 4;                       // entries per thread loaded ahead of the counts
     static_assert(kPer < 8, "finalize: a thread's kept count fits the three-bit scan");
     static_assert(kEntCap % kSelThreads == 0, "finalize: whole entries per thread");
-    static_assert(kSelMaxWgs * 16 == kSelThreads, "finalize: 16 threads per slice");
+    static_assert(kSelMaxWgs * 16 == kSelThreads, "finalize: at least 16 threads per slice");
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int nfb = a.L.fb_wgs;
     const int k = a.topk;
@@ -537,20 +537,24 @@ __device__ __forceinline__ void finalize_body(const SelectArgs &a, int xw, int r
     // (one workgroup per row, so none of them is wasted but for rows whose
     // keys are all selected, where the state and lists are stale and unused):
     // the bound, the state, the third digits, the per-slice counts and,
-    // without waiting for those, the first 64 entries of every slice (16
-    // threads per slice), which is all of a slice in the usual case.
+    // without waiting for those, the first kPre * tps entries of every slice
+    // (tps = 1024 / S rounded down to a power of two threads per slice: 64
+    // entries at 64 slices, 256 at 16), which is all of a slice in the usual
+    // case (a slice's share of the row's ~2,048 entries grows as S shrinks).
     const int b_raw = a.row_bound[r];
     const uint32_t *ecnt = (const uint32_t *)(a.ws + a.L.ent_cnt) + (int64_t)r * S;
     const uint32_t *ccnt = (const uint32_t *)(a.ws + a.L.cand_cnt) + (int64_t)r * S;
     const unsigned long long *sl = (const unsigned long long *)(a.ws + a.L.ent_list) + (int64_t)r * S * kSliceCap;
-    const int x = t >> 4, j0 = t & 15;
+    const int tsh = 10 - (S > 1 ? 32 - __builtin_clz((uint32_t)(S - 1)) : 0);   // log2(tps)
+    const int tps = 1 << tsh;
+    const int x = t >> tsh, j0 = t & (tps - 1);
     const int xs = x < S ? x : 0;
     const RowState st = ((const RowState *)(a.ws + a.L.state))[r];
     const uint32_t h3v = hist3[t & (kBins3 - 1)];
     const uint32_t ne = ecnt[lane < S ? lane : 0], ncx = ccnt[lane < S ? lane : 0];
     unsigned long long pre[kPre];
 #pragma unroll
-    for (int m = 0; m < kPre; ++m) pre[m] = sl[(int64_t)xs * kSliceCap + j0 + 16 * m];
+    for (int m = 0; m < kPre; ++m) pre[m] = sl[(int64_t)xs * kSliceCap + min(j0 + tps * m, kSliceCap - 1)];
     __builtin_amdgcn_sched_barrier(0);
     const int b = clamp_bound(b_raw, a.max_bound);
     bool overflow = false;        // heavy ties: the row takes the fallback
@@ -564,7 +568,7 @@ __device__ __forceinline__ void finalize_body(const SelectArgs &a, int xw, int r
         // past a slice's capacity or the row's send the row to the fallback
         if (wave == 0) {
             const uint32_t c = live ? ne : 0u, cc = live ? ncx : 0u;
-            const uint32_t rm = c > 16u * kPre ? c - 16u * kPre : 0u;
+            const uint32_t rm = c > (uint32_t)(tps * kPre) ? c - (uint32_t)(tps * kPre) : 0u;
             // a slice holding more entries than its capacity (possible only
             // with counters left dirty by a misused workspace) is never read
             // past its end: the row takes the fallback instead
@@ -596,9 +600,9 @@ __device__ __forceinline__ void finalize_body(const SelectArgs &a, int xw, int r
                 const int o = (int)offe[x], n = (int)(offe[x + 1] - offe[x]);
 #pragma unroll
                 for (int m = 0; m < kPre; ++m)
-                    if (j0 + 16 * m < n) ent[o + j0 + 16 * m] = pre[m];
+                    if (j0 + tps * m < n) ent[o + j0 + tps * m] = pre[m];
             }
-            // entries past the first 16*kPre of their slice (a short row puts
+            // entries past the first tps*kPre of their slice (a short row puts
             // all its entries in one or two slices): spread over every thread,
             // each finding its slice by a binary search of roff; all loads go
             // out before any is stored
@@ -616,7 +620,7 @@ __device__ __forceinline__ void finalize_body(const SelectArgs &a, int xw, int r
                             const int mid = (lo + hi + 1) >> 1;
                             if ((int)roff[mid] <= i) lo = mid; else hi = mid - 1;
                         }
-                        const int jj = 16 * kPre + (i - (int)roff[lo]);
+                        const int jj = tps * kPre + (i - (int)roff[lo]);
                         dst[m] = (int)offe[lo] + jj;
                         v[m] = sl[(int64_t)lo * kSliceCap + jj];
                     }
