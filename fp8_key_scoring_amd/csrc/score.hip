@@ -76,6 +76,11 @@ constexpr int kHistLds = (kScoreThreads / 64) * kGroupRows * kBins1 * kCntCopies
 constexpr int kBlockPieces = kGroupRows * kHeads * kDim / 8 / kScoreThreads;   // q pieces per thread, 4 rows
 // Word 3 of a raw buffer resource for 32-bit accesses (32-bit data format).
 constexpr int kBufferFlags = 0x00020000;
+// Cache policy of the score stores: sc1, written through to the device-coherent
+// level, so the kernel's end has no dirty score lines to write back from the
+// XCD's L2 before the selection kernels (on other XCDs) read them (C3: the
+// launch 48.5 -> 47.4 us, interleaved).
+constexpr int kScoreStorePolicy = 16;
 
 // Dynamic LDS: q of four rows, then the linear term's A operand.  q is read
 // only while a row group is set up; when counting, the same 64 KB then hold
@@ -145,6 +150,52 @@ __device__ __forceinline__ void stage_q(const ScoreArgs &a, int row0, int tid, u
     }
 }
 
+// The linear term's A operand for row slot ur of a group whose q starts at LDS
+// row slot q_slot: A row 4p + ur holds part p of u = sum_h (w[h]/2) q[h] (fp32),
+// split into three bf16 parts hi + mid + lo (each residual exact in fp32, so
+// the three carry u to fp32 precision).  One wave: lane l sums dims
+// 8 (l % 16) .. +7 over the sixteen heads whose halved weights it holds for
+// the epilogue, wh[hb][jj] for head 16 hb + 4 (l / 16) + jj -- one 16-byte LDS
+// read per head and eight independent fma chains -- and two permlane swap
+// rounds add the four lane rows' partial sums, after which lane row p (p < 3)
+// writes part p of its eight dims as one 16-byte store.
+__device__ __forceinline__ void linear_u(const unsigned char *lds_q, int q_slot, int ur, const f32x4_t (&wh)[4],
+                                         __bf16 *t1_lds, int lane) {
+    typedef __bf16 bf16x8l_t __attribute__((ext_vector_type(8)));
+    const int pc = lane & 15, lr4 = lane >> 4;
+    u32x4_t qv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        qv[i] = *(const u32x4_t *)(lds_q + q_lds_off(q_slot + ur, 16 * (i >> 2) + 4 * lr4 + (i & 3), pc));
+    float u[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u[e] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float w = wh[i >> 2][i & 3];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            u[2 * e] = fmaf(w, __uint_as_float(qv[i][e] << 16), u[2 * e]);
+            u[2 * e + 1] = fmaf(w, __uint_as_float(qv[i][e] & 0xffff0000u), u[2 * e + 1]);
+        }
+    }
+    bf16x8l_t part;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const auto a32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(u[e]), __float_as_uint(u[e]), false, false);
+        const float s2 = __uint_as_float(a32[0]) + __uint_as_float(a32[1]);
+        const auto a16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(s2), __float_as_uint(s2), false, false);
+        const float uu = __uint_as_float(a16[0]) + __uint_as_float(a16[1]);
+        const __bf16 hi = (__bf16)uu;
+        const float r1 = uu - (float)hi;
+        const __bf16 mid = (__bf16)r1;
+        const __bf16 lo = (__bf16)(r1 - (float)mid);
+        part[e] = lr4 == 0 ? hi : (lr4 == 1 ? mid : lo);
+    }
+    // dims 8pc .. 8pc+7: K step pc % 4 of the A operand, lane row pc / 4
+    if (lr4 < 3) *(bf16x8l_t *)(t1_lds + ((pc & 3) * 64 + lr4 * 4 + ur + 16 * (pc >> 2)) * 8) = part;
+}
+
 struct KeyGroup {
     u32x4_t lo, hi;   // 32 code bytes of key lane%16
     float scale;
@@ -178,7 +229,7 @@ struct WaveJob {
 template <int R, bool kHist, int kRing = ring_depth<R>()>
 __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j, unsigned char *lds_q,
                                            bf16_t *t1_lds, uint32_t *lds_cnt, int q_slot, bool staged,
-                                           float w_blk) {
+                                           bool u_ready) {
     const int lane = j.lane;
     const int kig = lane & 15;      // key of the group this lane loads / scores
     const int lrow = lane >> 4;     // lane row: 32-byte quarter of the key, 4-head slice of D
@@ -239,58 +290,34 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
                     qa[r][hb][ks] = *(const bf16x8_t *)(lds_q + q_lds_off(q_slot + r, 16 * hb + kig, 4 * lrow + ks));
-        // The linear term's A operand: A row 4p + r holds part p of
-        // u_r = (1/2) sum_h w[r][h] q[r][h] (fp32, heads in order), split
-        // into three bf16 parts hi + mid + lo (each residual exact in fp32,
-        // so the three carry u_r to fp32 precision); the other rows are zero.
-        // Wave q_slot + r computes row r, lane l dims 2l and 2l+1, from q in
-        // LDS and w[r][h] broadcast from lane h, through LDS ([ks][lane][8]).
+        // The linear term's A operand (linear_u): wave q_slot + r builds row
+        // r's, unless the kernel built it while the page ids were in flight.
         const int ur = wave_idx - q_slot;
-        if (ur >= 0 && ur < R) {
-            const float w_lane = staged ? w_blk : a.w[(int64_t)(j.row0 + ur) * kHeads + lane];
-            const unsigned char *qr = lds_q + q_lds_off(q_slot + ur, 0, 0);
-            float u0 = 0.0f, u1 = 0.0f;
+        if (!u_ready && ur >= 0 && ur < R) {
+            f32x4_t wq[4];
 #pragma unroll
-            for (int h0 = 0; h0 < kHeads; h0 += 8) {
-                uint32_t qw[8];
+            for (int hb = 0; hb < 4; ++hb) {
+                wq[hb] = wv[0][hb];
 #pragma unroll
-                for (int h = 0; h < 8; ++h)   // dims 2l, 2l+1 of head h0+h: one 4-byte read
-                    qw[h] = *(const uint32_t *)(qr + q_lds_off(0, h0 + h, lane >> 2) + (lane & 3) * 4);
-#pragma unroll
-                for (int h = 0; h < 8; ++h) {
-                    const float wh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), h0 + h));
-                    u0 = fmaf(wh, __uint_as_float(qw[h] << 16), u0);
-                    u1 = fmaf(wh, __uint_as_float(qw[h] & 0xffff0000u), u1);
-                }
+                for (int r = 1; r < R; ++r) wq[hb] = ur == r ? wv[r][hb] : wq[hb];
             }
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const float u = (e ? u1 : u0) * 0.5f;
-                const int d = 2 * lane + e;
-                const bf16_t hi = (bf16_t)u;
-                const float r1 = u - (float)hi;
-                const bf16_t mid = (bf16_t)r1;
-                const bf16_t lo = (bf16_t)(r1 - (float)mid);
-                const int ks = (d & 31) >> 3, lr = d >> 5;
-                t1_lds[(ks * 64 + 0 * 4 + ur + 16 * lr) * 8 + (d & 7)] = hi;
-                t1_lds[(ks * 64 + 1 * 4 + ur + 16 * lr) * 8 + (d & 7)] = mid;
-                t1_lds[(ks * 64 + 2 * 4 + ur + 16 * lr) * 8 + (d & 7)] = lo;
-            }
+            linear_u(lds_q, q_slot, ur, wq, t1_lds, lane);
         }
-        lds_barrier();
+        lds_barrier();   // u is written; every wave is done reading q from LDS
+        if (kHist) {     // the q region becomes the counters
+            u32x4_t *c4 = (u32x4_t *)lds_cnt;
+            const uint32_t z = (uint32_t)tid >> 16;   // 0, built here rather than kept live
+            for (int i = tid; i < kHistLds / 4; i += kScoreThreads) c4[i] = u32x4_t{z, z, z, z};
+        }
         const bool t1_row = (kig >> 2) < 3 && (kig & 3) < R;   // this lane's A row is used
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const bf16x8_t v = *(const bf16x8_t *)(t1_lds + (ks * 64 + lane) * 8);
             t1a[ks] = t1_row ? v : bf16x8_t{};
         }
-        lds_barrier();   // t1_lds may be written again by the next row group
-        if (kHist) {   // every wave is done with q in LDS: the region becomes the counters
-            u32x4_t *c4 = (u32x4_t *)lds_cnt;
-            const uint32_t z = (uint32_t)tid >> 16;   // 0, built here rather than kept live
-            for (int i = tid; i < kHistLds / 4; i += kScoreThreads) c4[i] = u32x4_t{z, z, z, z};
-            lds_barrier();
-        }
+        // t1_lds may be written again by the next row group, and the
+        // counters are clear before any wave adds to them
+        lds_barrier();
     }
     if (j.n_my == 0) return;
     // q lives in AGPRs: the MFMA reads its A operand from there directly,
@@ -374,7 +401,7 @@ __device__ __forceinline__ void score_rows(const ScoreArgs &a, const WaveJob &j,
             const __amdgpu_buffer_rsrc_t row =
                 __builtin_amdgcn_make_buffer_rsrc((void *)(a.scores + (int64_t)(j.row0 + r) * a.sstride + j.c0),
                                                   0, nrec, kBufferFlags);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), row, in_job ? (s - j.c0) * 4 : nrec, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), row, in_job ? (s - j.c0) * 4 : nrec, 0, kScoreStorePolicy);
             if (kHist) {   // every lane adds: 1 for a stored score, else 0 (no branch)
                 const uint32_t d = radix_key(out) >> kDigit1Shift;
                 atomicAdd(lds_cnt + (((j.tid >> 6) * kGroupRows + r) * kBins1 + d) * kCntCopies + lane % kCntCopies,
@@ -484,7 +511,11 @@ void score_kernel(ScoreArgs a) {
             qt_blk[c] = *(gptr<u32x4_t>)(a.q + ((int64_t)(yb + (c >> 2)) * kHeads + ((ci >> 4) & 63)) * kDim +
                                          8 * (ci & 15));
     }
-    const float w_blk = a.w[(int64_t)min(yb + wave, a.rows - 1) * kHeads + lane];
+    // halved w of block row `wave` as linear_u takes it (heads 16 hb + 4 (lane / 16) + jj)
+    f32x4_t wq_blk[4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb)
+        wq_blk[hb] = *(gptr<f32x4_t>)(a.w + (int64_t)min(yb + wave, a.rows - 1) * kHeads + 16 * hb + 4 * (lane >> 4)) * 0.5f;
     __builtin_amdgcn_sched_barrier(0);
     v_bnd = v_bnd < 0 ? 0 : (v_bnd > a.max_bound ? a.max_bound : v_bnd);
     // row `back` starts a run when it is row 0 or differs from row back-1
@@ -549,6 +580,10 @@ void score_kernel(ScoreArgs a) {
             if ((c >> 2) < rows_blk) *(u32x4_t *)(lds_q + q_lds_off(ci >> 10, (ci >> 4) & 63, ci & 15)) = qt_blk[c];
         }
         lds_barrier();   // (the page ids may still be in flight)
+        // the first group's linear term while the page ids are in flight:
+        // block row `wave` is row wave - bi_first of the group
+        const int ur = wave - bi_first;
+        if (ur >= 0 && ur < rg_first) linear_u(lds_q, bi_first, ur, wq_blk, t1_lds, lane);
     }
 
     for (int bi = bi_first; bi < kGroupRows; ++bi) {
@@ -588,12 +623,12 @@ void score_kernel(ScoreArgs a) {
         const bool staged = bi == bi_first && staged_first;
         const int q_slot = staged ? bi : 0;
         switch (nrows) {   // every wave, also one with no groups (q staging)
-        case 4: score_rows<4, kHist>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, w_blk); break;
-        case 3: score_rows<3, kHist>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, w_blk); break;
-        case 2: score_rows<2, kHist>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, w_blk); break;
+        case 4: score_rows<4, kHist>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, staged); break;
+        case 3: score_rows<3, kHist>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, staged); break;
+        case 2: score_rows<2, kHist>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, staged); break;
         default:
-            if (job.n_my >= kDeepRingGroups) score_rows<1, kHist>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, w_blk);
-            else score_rows<1, kHist, 4>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, w_blk);
+            if (job.n_my >= kDeepRingGroups) score_rows<1, kHist>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, staged);
+            else score_rows<1, kHist, 4>(a, job, lds_q, t1_lds, lds_cnt, q_slot, staged, staged);
             break;
         }
 
@@ -662,7 +697,7 @@ void score_row_kernel(ScoreArgs a) {
     f32x4_t wv[4];
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) wv[hb] = *(gptr<f32x4_t>)(a.w + 16 * hb + 4 * lrow) * 0.5f;
-    const float w_lane = a.w[lane];
+
     __builtin_amdgcn_sched_barrier(0);
     bnd = bnd < 0 ? 0 : (bnd > a.max_bound ? a.max_bound : bnd);
     const int c0 = blockIdx.x * a.chunk;
@@ -700,49 +735,21 @@ void score_row_kernel(ScoreArgs a) {
 #pragma unroll
     for (int p = 0; p < kRowRing; ++p) load_group(p, kb[p]);
 
-    // q to LDS, then back in MFMA A-operand order into AGPRs
+    // q to LDS; the last wave builds the linear term's A operand (as in
+    // score_rows, with one row: A row 4p holds part p of u) before its own q
+    // read-back; then q goes back in MFMA A-operand order into AGPRs
 #pragma unroll
     for (int c = 0; c < kPieces; ++c) {
         const int ci = tid + c * kRowThreads;
         *(u32x4_t *)(lds_q + q_lds_off(0, ci >> 4, ci & 15)) = qt[c];
     }
     lds_barrier();
+    if (wave == kRowWaves - 1) linear_u(lds_q, 0, 0, wv, t1_lds, lane);
     bf16x8_t qa[4][4];
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) qa[hb][ks] = *(const bf16x8_t *)(lds_q + q_lds_off(0, 16 * hb + kig, 4 * lrow + ks));
-    // the linear term's A operand (as in score_rows, with one row): A row 4p
-    // holds part p (hi, mid, lo bf16) of u = (1/2) sum_h w_h q_h, computed
-    // by the last wave, lane l dims 2l and 2l+1
-    if (wave == kRowWaves - 1) {
-        float u0 = 0.0f, u1 = 0.0f;
-#pragma unroll
-        for (int h0 = 0; h0 < kHeads; h0 += 8) {
-            uint32_t qw[8];
-#pragma unroll
-            for (int h = 0; h < 8; ++h) qw[h] = *(const uint32_t *)(lds_q + q_lds_off(0, h0 + h, lane >> 2) + (lane & 3) * 4);
-#pragma unroll
-            for (int h = 0; h < 8; ++h) {
-                const float wh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), h0 + h));
-                u0 = fmaf(wh, __uint_as_float(qw[h] << 16), u0);
-                u1 = fmaf(wh, __uint_as_float(qw[h] & 0xffff0000u), u1);
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const float u = (e ? u1 : u0) * 0.5f;
-            const int d = 2 * lane + e;
-            const bf16_t hi = (bf16_t)u;
-            const float r1 = u - (float)hi;
-            const bf16_t mid = (bf16_t)r1;
-            const bf16_t lo = (bf16_t)(r1 - (float)mid);
-            const int ks = (d & 31) >> 3, lr = d >> 5;
-            t1_lds[(ks * 64 + 0 + 16 * lr) * 8 + (d & 7)] = hi;
-            t1_lds[(ks * 64 + 4 + 16 * lr) * 8 + (d & 7)] = mid;
-            t1_lds[(ks * 64 + 8 + 16 * lr) * 8 + (d & 7)] = lo;
-        }
-    }
     lds_barrier();   // q in LDS is read and u is written
     bf16x8_t t1a[4];
     {
@@ -815,7 +822,7 @@ void score_row_kernel(ScoreArgs a) {
             const float out = reduce4(P[0], P[1], P[2], P[3]) * sv;
             const int s = group(ip) * kKeysPerMfma + lane;
             const bool in_job = ip + lrow < n_my;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), out_row, in_job ? (s - c0) * 4 : nrec, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), out_row, in_job ? (s - c0) * 4 : nrec, 0, kScoreStorePolicy);
             if (kHist) {
                 const uint32_t d = radix_key(out) >> kDigit1Shift;
                 atomicAdd(lds_cnt + (wave * kBins1 + d) * kCntCopies + lane % kCntCopies, (in_job && s < bnd) ? 1u : 0u);
