@@ -4,7 +4,10 @@ Workload: one request's 4 verify rows over 524,288 paged E4M3 keys (bounds
 n-3..n), 64 heads x 128, page 64, top-2048.  A step is one indexer_launch
 call.  Inputs sit in HBM before timing starts; the timed steps rotate over
 several copies of the key pool and page table (together larger than the
-256 MB MALL) so each step streams its keys from HBM.
+256 MB MALL) so each step streams its keys from HBM.  Before the warmup
+steps the launch runs back to back, untimed, for --settle seconds, so the
+timed steps run at the GPU's sustained clocks rather than in the first tens
+of milliseconds after idle (the count is reported as settle_launches).
 
 Prints one JSON line.  Extra keys: "roofline" for the launch's scoring kernel
 (timed per launch with HIP events on the launch stream, through the launch's
@@ -40,6 +43,9 @@ def parse():
     ap.add_argument("--config", type=int, default=3, help="workload 1..8 (3 = 512K keys x 4 rows)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of back-to-back untimed launches before the warmup steps, so the "
+                         "timed steps run at the GPU's sustained clocks (0: none)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip measuring the device's HBM and MFMA peaks (profiled runs)")
     ap.add_argument("--shards", type=int, default=0,
@@ -491,10 +497,26 @@ def main():
     outs = torch.empty((p.rows, p.topk), dtype=torch.int32, device=dev)
     scores = torch.empty((p.rows, mb), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    # the device's own peaks are measured first: seconds of full-load work
+    # that also bring the GPU's clocks to their sustained level (from idle,
+    # back-to-back launches take ~30 ms to settle: 52-56 us per launch in the
+    # first blocks of 20, ~47 us after ~600 launches, on one box)
+    peaks = None if args.no_peaks else measured_peaks(torch, dev)
 
     def step(i):
         fk.indexer_launch(**pools[i % len(pools)], max_bound=mb, topk=p.topk, out_idx=outs, workspace=ws)
 
+    # Clock settling (untimed, reported as settle_launches / settle_s): from
+    # idle, back-to-back launches slow down the first tens of milliseconds
+    # (C3 on one box: 51-56 us per launch in the first blocks, ~47 us after
+    # ~600 launches), so short timed blocks would measure the ramp
+    n_settle, t_settle = 0, time.time()
+    while time.time() - t_settle < args.settle:
+        for i in range(100):
+            step(i)
+        n_settle += 100
+        torch.cuda.synchronize()
+    t_settle = time.time() - t_settle
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -611,8 +633,7 @@ def main():
                  "hbm_gbs_at_kernel_time": round(ach_gbs, 1),
                  "mfma_busy_frac": prof.get("mfma_busy_frac"),
                  "score_only_kernel_us": round(score_only_us, 2)})
-    if not args.no_peaks:
-        peaks = measured_peaks(torch, dev)
+    if peaks is not None:
         mpeak = peaks["bf16_mfma_TFLOPs"] if mfma_bound else peaks["hbm_read_GBs"]
         roof.update({"measured_peak": mpeak, "frac_of_measured_peak": round(roof["achieved"] / mpeak, 4),
                      "measured_peaks": peaks})
@@ -626,6 +647,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "settle_launches": n_settle,
+        "settle_s": round(t_settle, 3),
         "us_per_launch": ms_step * 1e3,
         "us_per_launch_hot": ms_step_hot * 1e3,
         "us_per_launch_graph": None if us_graph is None else round(us_graph, 2),
