@@ -10,8 +10,8 @@ timed steps run at the GPU's sustained clocks rather than in the first tens
 of milliseconds after idle (the count is reported as settle_launches).
 
 Prints one JSON line.  Extra keys: "roofline" for the launch's scoring kernel
-(timed inside launches with HIP events on the launch stream around the
-launch's scoring stage indexer_launch_score) and "cpu_baseline" (the CPU oracle on the
+(timed inside launches with HIP events on the launch stream after each of
+the launch's two stages, less the events' own overhead) and "cpu_baseline" (the CPU oracle on the
 same workload, or a bounded sample of it, as processes on the host's cores
 and on one core).
 """
@@ -593,32 +593,40 @@ def main():
 
     # the launch's scoring kernel as the timed launch runs it: n_k launches,
     # each as its two stages (indexer_launch_score then indexer_launch_select,
-    # which together are indexer_launch), with events recorded on the launch
-    # stream right before and after the scoring stage; the mean of those
-    # intervals is the kernel's average duration inside launches.  Back to
-    # back, with no selection between them, the same kernel runs slower
-    # (score_stage_back_to_back_us): the MFMA pipes are power-limited, and in
-    # a launch the selection kernels let the chip recover.
+    # which together are indexer_launch), with an event recorded on the launch
+    # stream after each stage.  An event between two kernels exposes the
+    # second one's dispatch (~2 us), which back-to-back kernels of one launch
+    # hide, so each interval carries one marker's overhead d: the mean launch
+    # with the two markers is a plain launch (timed right before) + 2d, and the kernel's
+    # duration is the mean scoring interval - d (both intervals and d are
+    # reported).  Back to back, with no selection between them, the same
+    # kernel runs slower (score_stage_back_to_back_us): the MFMA pipes are
+    # power-limited, and in a launch the selection kernels let the chip
+    # recover.
     n_k = max(20, min(args.steps, 200))
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_k)]
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_k)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_k + 1)]
 
-    def staged(i, evs=None):
+    def staged(i, ev_mid=None, ev_end=None):
         pi = pools[i % len(pools)]
-        if evs:
-            evs[0].record(stream)
         fk.indexer_launch_score(**pi, max_bound=mb, topk=p.topk, workspace=ws)
-        if evs:
-            evs[1].record(stream)
+        if ev_mid is not None:
+            ev_mid.record(stream)
         fk.indexer_launch_select(pi["row_bound"], max_bound=mb, topk=p.topk, out_idx=outs, workspace=ws)
+        if ev_end is not None:
+            ev_end.record(stream)
 
     for i in range(args.warmup):
         staged(i)
-    torch.cuda.synchronize()
+    # the reference launch time, right before the staged block (same state)
+    launch_ref_us = block_us(step, n_k)
+    evs[0].record(stream)
     for i in range(n_k):
-        staged(i, (ev_a[i], ev_b[i]))
+        staged(i, evs[2 * i + 1], evs[2 * i + 2])
     torch.cuda.synchronize()
-    score_ms = float(np.mean([ev_a[i].elapsed_time(ev_b[i]) for i in range(n_k)]))
+    score_iv = float(np.mean([evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(n_k)])) * 1e3
+    select_iv = float(np.mean([evs[2 * i + 1].elapsed_time(evs[2 * i + 2]) for i in range(n_k)])) * 1e3
+    marker_us = max(0.0, (score_iv + select_iv - launch_ref_us) / 2)
+    score_ms = (score_iv - marker_us) * 1e-3
     # the same stage back to back (its digit counts pile up in a workspace of
     # its own, cleared afterwards), for comparison
     ws_t = fk.new_workspace(prob, True, dev)
@@ -650,12 +658,15 @@ def main():
             {"bound": "hbm", "achieved": round(ach_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
              "frac": round(ach_gbs / PEAK_HBM_GBS, 4), "traffic": traffic})
     roof.update({"kernel": "the scoring kernel of indexer_launch (with the selection's digit counts), "
-                           "timed inside launches run as their two stages (events around indexer_launch_score)",
+                           "timed inside launches run as their two stages: the scoring interval between "
+                           "events, less one event marker's overhead",
                  "kernel_us": round(score_ms * 1e3, 2), "traffic_unit": "bytes per launch",
                  "algorithmic_flops": flops, "algorithmic_bytes": abytes,
                  "hbm_gbs_at_kernel_time": round(ach_gbs, 1),
                  "mfma_busy_frac": prof.get("mfma_busy_frac"),
                  "score_only_kernel_us": round(score_only_us, 2),
+                 "score_stage_interval_us": round(score_iv, 2), "select_stage_interval_us": round(select_iv, 2),
+                 "marker_overhead_us": round(marker_us, 2), "launch_ref_us": round(launch_ref_us, 2),
                  "score_stage_back_to_back_us": round(score_b2b_us, 2)})
     if peaks is not None:
         mpeak = peaks["bf16_mfma_TFLOPs"] if mfma_bound else peaks["hbm_read_GBs"]
