@@ -135,20 +135,32 @@ def host_cpus():
 
 
 def cpu_model():
-    """The host CPU's model name (lscpu's, else /proc/cpuinfo's)."""
+    """The host CPU's model name (lscpu's, else /proc/cpuinfo's), with the
+    x86 family / model / stepping numbers from /proc/cpuinfo (a virtualised
+    host may report only a generic name such as "AMD EPYC")."""
     import subprocess
+    name = ""
     try:
         out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
         for line in out.splitlines():
             if line.startswith("Model name:"):
-                return line.split(":", 1)[1].strip()
+                name = line.split(":", 1)[1].strip()
+                break
     except (OSError, subprocess.SubprocessError):
         pass
+    ids = {}
     try:
         with open("/proc/cpuinfo") as f:
-            return next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+            for line in f:
+                if not line.strip():
+                    break   # the first processor's block
+                k, _, v = line.partition(":")
+                ids[k.strip()] = v.strip()
     except OSError:
-        return ""
+        pass
+    name = name or ids.get("model name", "")
+    fms = [f"{k} {ids[k]}" for k in ("cpu family", "model", "stepping") if k in ids]
+    return f"{name} ({', '.join(fms)})" if fms else name
 
 
 _CPU_PROBLEM = None   # the workload, inherited by the forked oracle workers
