@@ -520,7 +520,7 @@ def main():
 
     # Clock settling (untimed, reported as settle_launches / settle_s): from
     # idle, back-to-back launches slow down the first tens of milliseconds
-    # (C3 on one box: 51-56 us per launch in the first blocks, ~47 us after
+    # (4 rows x 524,288 keys on one box: 51-56 us per launch in the first blocks, ~47 us after
     # ~600 launches), so short timed blocks would measure the ramp
     n_settle, t_settle = 0, time.time()
     while time.time() - t_settle < args.settle:

@@ -78,8 +78,8 @@ constexpr int kBlockPieces = kGroupRows * kHeads * kDim / 8 / kScoreThreads;   /
 constexpr int kBufferFlags = 0x00020000;
 // Cache policy of the score stores: sc1, written through to the device-coherent
 // level, so the kernel's end has no dirty score lines to write back from the
-// XCD's L2 before the selection kernels (on other XCDs) read them (C3: the
-// launch 48.5 -> 47.4 us, interleaved).
+// XCD's L2 before the selection kernels (on other XCDs) read them (4 rows x
+// 524,288 keys: the launch 48.5 -> 47.4 us, interleaved).
 constexpr int kScoreStorePolicy = 16;
 
 // Dynamic LDS: q of four rows, then the linear term's A operand.  q is read

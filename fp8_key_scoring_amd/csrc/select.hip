@@ -188,7 +188,7 @@ __device__ __forceinline__ void hist1_body(const SelectArgs &a, int x, int r) {
 // Second-digit counts inside the first-digit bin of the k-th largest key.
 // Four LDS copies (wave % 4) keep the waves' atomics apart; with one copy per
 // wave the zeroing and the final sum over 16 copies cost more than the
-// collisions they avoid (C5's launch 3 us longer).
+// collisions they avoid (256 rows of 8K-262K keys: the launch 3 us longer).
 __device__ __forceinline__ void refine_body(const SelectArgs &a, int x, int r) {
     __shared__ uint32_t h1[kBins1];
     __shared__ uint32_t h2[4][kBins2];
