@@ -1,8 +1,8 @@
 """Pins of the sparse-attention oracle (oracle_sparse_attention in oracle.c),
 the step after the indexer: each row's 16 heads attend over its selected key
-positions in a paged latent cache (the reading is stated in oracle.c and
-the design doc; the pages give no formula, so every pin here is a closed form of
-softmax attention, not a restatement of the oracle's code):
+positions in a paged latent cache (the reading is stated in oracle.c; the
+pages give no formula, so every pin here is a closed form of softmax
+attention, not a restatement of the oracle's code):
 
   * one selected key returns that key's first 512 values, lse = its logit;
   * equal logits return the mean of the values, lse = log(count);
