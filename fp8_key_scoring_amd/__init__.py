@@ -157,15 +157,23 @@ def _problem_from(q, k_e4m3, page_table, max_bound: int, topk: int, score_stride
 
 
 def _check_inputs(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound):
+    # (torch.Size compares equal to a tuple; one chained condition per
+    # tensor keeps the per-call cost low for launch-rate callers)
     import torch
-    R = q.shape[0]
-    assert q.dtype == torch.bfloat16 and tuple(q.shape[1:]) == (HEADS, HEAD_DIM) and q.is_contiguous()
-    assert w.dtype == torch.float32 and tuple(w.shape) == (R, HEADS) and w.is_contiguous()
-    assert k_e4m3.dtype == torch.uint8 and tuple(k_e4m3.shape[1:]) == (PAGE, HEAD_DIM) and k_e4m3.is_contiguous()
-    assert k_scale.dtype == torch.float32 and tuple(k_scale.shape) == (k_e4m3.shape[0], PAGE) and k_scale.is_contiguous()
+    qs = q.shape
+    R = qs[0]
+    assert q.dtype == torch.bfloat16 and qs[1:] == (HEADS, HEAD_DIM) and q.is_contiguous()
+    assert w.dtype == torch.float32 and w.shape == (R, HEADS) and w.is_contiguous()
+    ks = k_e4m3.shape
+    assert k_e4m3.dtype == torch.uint8 and ks[1:] == (PAGE, HEAD_DIM) and k_e4m3.is_contiguous()
+    assert k_scale.dtype == torch.float32 and k_scale.shape == (ks[0], PAGE) and k_scale.is_contiguous()
     assert page_table.dtype == torch.int32 and page_table.dim() == 2 and page_table.is_contiguous()
-    assert row_pt.dtype == torch.int32 and tuple(row_pt.shape) == (R,) and row_pt.is_contiguous()
-    assert row_bound.dtype == torch.int32 and tuple(row_bound.shape) == (R,) and row_bound.is_contiguous()
+    assert row_pt.dtype == torch.int32 and row_pt.shape == (R,) and row_pt.is_contiguous()
+    assert row_bound.dtype == torch.int32 and row_bound.shape == (R,) and row_bound.is_contiguous()
+    dev = q.device
+    assert dev.type == "cuda" and w.device == dev and k_e4m3.device == dev and k_scale.device == dev \
+        and page_table.device == dev and row_pt.device == dev and row_bound.device == dev, \
+        "every input must be on one GPU"
 
 
 def _check_scores(scores, rows: int, max_bound: int, device) -> None:
@@ -177,15 +185,15 @@ def _check_scores(scores, rows: int, max_bound: int, device) -> None:
     assert scores.dim() == 2 and scores.stride(1) == 1, "scores must be 2-D with unit inner stride"
     assert scores.shape[0] >= rows and scores.shape[1] >= max_bound, \
         f"scores {tuple(scores.shape)} too small for {rows} rows x {max_bound} keys"
-    assert scores.device == torch.device(device), "scores must be on the inputs' device"
+    assert scores.device == device, "scores must be on the inputs' device"
 
 
 def _check_out(out_idx, rows: int, topk: int, device) -> None:
     """out_idx must be a contiguous int32 [rows, topk] tensor on the inputs' device."""
     import torch
     assert out_idx.dtype == torch.int32 and out_idx.is_contiguous(), "out_idx must be contiguous int32"
-    assert tuple(out_idx.shape) == (rows, topk), f"out_idx must be ({rows}, {topk}), got {tuple(out_idx.shape)}"
-    assert out_idx.device == torch.device(device), "out_idx must be on the inputs' device"
+    assert out_idx.shape == (rows, topk), f"out_idx must be ({rows}, {topk}), got {tuple(out_idx.shape)}"
+    assert out_idx.device == device, "out_idx must be on the inputs' device"
 
 
 def indexer_score(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound, *, max_bound: int,

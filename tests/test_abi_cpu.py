@@ -278,3 +278,23 @@ def test_header_is_plain_c_and_links(tmp_path):
            "-o", str(exe), lib, "-Wl,-rpath," + os.path.dirname(lib)]
     out = subprocess.run(cmd, capture_output=True, text=True)
     assert out.returncode == 0, out.stderr[-2000:]
+
+
+def test_binding_rejects_host_tensors_before_any_call(lib):
+    """The binding passes raw pointers: inputs that are not all on one GPU
+    (here host tensors) are refused before the library is called."""
+    import torch
+    import fp8_key_scoring_amd as fk
+    R = 2
+    q = torch.zeros(R, fk.HEADS, fk.HEAD_DIM, dtype=torch.bfloat16)
+    w = torch.zeros(R, fk.HEADS)
+    k = torch.zeros(4, fk.PAGE, fk.HEAD_DIM, dtype=torch.uint8)
+    ks = torch.zeros(4, fk.PAGE)
+    pt = torch.zeros(1, 4, dtype=torch.int32)
+    rp = torch.zeros(R, dtype=torch.int32)
+    rb = torch.full((R,), 100, dtype=torch.int32)
+    for fn in (fk.indexer_score, fk.indexer_launch, fk.indexer_launch_static):
+        with pytest.raises(AssertionError, match="one GPU"):
+            fn(q, w, k, ks, pt, rp, rb, max_bound=100)
+    with pytest.raises(AssertionError, match="one GPU"):
+        fk.indexer_launch_score(q, w, k, ks, pt, rp, rb, max_bound=100, workspace=torch.zeros(256, dtype=torch.uint8))
