@@ -170,9 +170,14 @@ def _check_inputs(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound):
     assert page_table.dtype == torch.int32 and page_table.dim() == 2 and page_table.is_contiguous()
     assert row_pt.dtype == torch.int32 and row_pt.shape == (R,) and row_pt.is_contiguous()
     assert row_bound.dtype == torch.int32 and row_bound.shape == (R,) and row_bound.is_contiguous()
-    dev = q.device
-    assert dev.type == "cuda" and w.device == dev and k_e4m3.device == dev and k_scale.device == dev \
-        and page_table.device == dev and row_pt.device == dev and row_bound.device == dev, \
+    _on_one_gpu(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound)
+
+
+def _on_one_gpu(first, *others) -> None:
+    """The library takes raw device pointers: every tensor given (None
+    skipped) must live on the first one's GPU."""
+    dev = first.device
+    assert dev.type == "cuda" and all(t is None or t.device == dev for t in others), \
         "every input must be on one GPU"
 
 
@@ -219,7 +224,7 @@ def indexer_topk(scores, row_bound, *, max_bound: int, topk: int = MAX_TOPK, out
     R = row_bound.shape[0]
     assert row_bound.dtype == torch.int32 and row_bound.is_contiguous()
     _check_scores(scores, R, max_bound, scores.device)
-    assert row_bound.device == scores.device, "row_bound must be on the scores' device"
+    _on_one_gpu(scores, row_bound, out_idx, workspace)
     prob = make_problem(rows=R, num_pages=1, pt_rows=1, pt_stride=max(1, (max_bound + 63) // 64),
                         max_bound=max_bound, topk=topk, score_stride=scores.stride(0))
     if out_idx is None:
@@ -248,6 +253,7 @@ def indexer_launch(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound, *, max_
     _check_out(out_idx, R, topk, q.device)
     if workspace is None:
         workspace = new_workspace(prob, scores is None, q.device)
+    _on_one_gpu(q, workspace)
     _check(load_library().indexer_launch(ctypes.byref(prob), _ptr(q), _ptr(w), _ptr(k_e4m3),
                                          _ptr(k_scale), _ptr(page_table), _ptr(row_pt),
                                          _ptr(row_bound), _ptr(scores), _ptr(out_idx),
@@ -268,6 +274,7 @@ def indexer_launch_score(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound, *
         _check_scores(scores, R, max_bound, q.device)
     sstride = scores.stride(0) if scores is not None else 0
     prob = _problem_from(q, k_e4m3, page_table, max_bound, topk, sstride)
+    _on_one_gpu(q, workspace)
     _check(load_library().indexer_launch_score(ctypes.byref(prob), _ptr(q), _ptr(w), _ptr(k_e4m3),
                                                _ptr(k_scale), _ptr(page_table), _ptr(row_pt),
                                                _ptr(row_bound), _ptr(scores), _ptr(workspace),
@@ -287,6 +294,7 @@ def indexer_launch_select(row_bound, *, max_bound: int, topk: int = MAX_TOPK, sc
     if out_idx is None:
         out_idx = torch.empty((R, topk), dtype=torch.int32, device=row_bound.device)
     _check_out(out_idx, R, topk, row_bound.device)
+    _on_one_gpu(row_bound, workspace)
     prob = make_problem(rows=R, num_pages=1, pt_rows=1, pt_stride=max(1, (max_bound + 63) // 64),
                         max_bound=max_bound, topk=topk,
                         score_stride=scores.stride(0) if scores is not None else 0)
@@ -337,6 +345,7 @@ def indexer_validate(page_table, row_pt, row_bound, *, max_bound: int, num_pages
     assert row_bound.dtype == torch.int32 and tuple(row_bound.shape) == (R,) and row_bound.is_contiguous()
     if status is None:
         status = torch.empty(1, dtype=torch.int32, device=row_pt.device)
+    _on_one_gpu(row_pt, page_table, row_bound, status)
     prob = make_problem(rows=R, num_pages=num_pages, pt_rows=page_table.shape[0], pt_stride=page_table.shape[1],
                         max_bound=max_bound, topk=MAX_TOPK, score_stride=0)
     _check(load_library().indexer_validate(ctypes.byref(prob), _ptr(page_table), _ptr(row_pt), _ptr(row_bound),
@@ -361,6 +370,7 @@ def indexer_write_keys(k_new, k_e4m3, k_scale, page_table, row_pt, row_bound, *,
     assert page_table.dtype == torch.int32 and page_table.dim() == 2 and page_table.is_contiguous()
     assert row_pt.dtype == torch.int32 and tuple(row_pt.shape) == (R,) and row_pt.is_contiguous()
     assert row_bound.dtype == torch.int32 and tuple(row_bound.shape) == (R,) and row_bound.is_contiguous()
+    _on_one_gpu(k_new, k_e4m3, k_scale, page_table, row_pt, row_bound)
     prob = make_problem(rows=R, num_pages=k_e4m3.shape[0], pt_rows=page_table.shape[0],
                         pt_stride=page_table.shape[1], max_bound=max_bound, topk=MAX_TOPK, score_stride=0)
     _check(load_library().indexer_write_keys(ctypes.byref(prob), _ptr(k_new), _ptr(k_e4m3), _ptr(k_scale),
@@ -386,6 +396,7 @@ def indexer_launch_new_keys(q, w, k_new, k_e4m3, k_scale, page_table, row_pt, ro
     _check_out(out_idx, R, topk, q.device)
     if workspace is None:
         workspace = new_workspace(prob, scores is None, q.device)
+    _on_one_gpu(q, k_new, workspace)
     _check(load_library().indexer_launch_new_keys(ctypes.byref(prob), _ptr(q), _ptr(w), _ptr(k_new),
                                                   _ptr(k_e4m3), _ptr(k_scale), _ptr(page_table),
                                                   _ptr(row_pt), _ptr(row_bound), _ptr(scores),
@@ -408,7 +419,11 @@ def indexer_shard_candidates(scores, out_idx, *, shard: int, shards: int, max_bo
         cand_score = torch.empty((R, shards * k), dtype=torch.float32, device=scores.device)
     if cand_idx is None:
         cand_idx = torch.empty((R, shards * k), dtype=torch.int32, device=scores.device)
+    assert scores.shape[0] >= R and scores.shape[1] >= max_bound, "scores too small for the shard's rows"
+    assert cand_score.dtype == torch.float32 and cand_idx.dtype == torch.int32
+    assert cand_score.shape == (R, shards * k) and cand_idx.shape == (R, shards * k)
     assert cand_score.is_contiguous() and cand_idx.is_contiguous()
+    _on_one_gpu(scores, out_idx, cand_score, cand_idx)
     prob = make_problem(rows=R, num_pages=1, pt_rows=1, pt_stride=max(1, (max_bound + 63) // 64),
                         max_bound=max_bound, topk=k, score_stride=scores.stride(0))
     _check(load_library().indexer_shard_candidates(ctypes.byref(prob), shard, shards, _ptr(scores),
@@ -428,6 +443,8 @@ def indexer_merge_topk(cand_score, cand_idx, *, shards: int, topk: int = MAX_TOP
     assert cand_idx.numel() == R * shards * topk and cand_score.numel() == R * shards * topk
     if out_idx is None:
         out_idx = torch.empty((R, topk), dtype=torch.int32, device=cand_idx.device)
+    assert out_idx.dtype == torch.int32 and out_idx.shape == (R, topk) and out_idx.is_contiguous()
+    _on_one_gpu(cand_idx, cand_score, out_idx)
     prob = make_problem(rows=R, num_pages=1, pt_rows=1, pt_stride=1, max_bound=0, topk=topk)
     _check(load_library().indexer_merge_topk(ctypes.byref(prob), shards, _ptr(cand_score), _ptr(cand_idx),
                                              _ptr(out_idx), _stream(cand_idx.device)))
@@ -472,6 +489,7 @@ def indexer_sparse_attention(q_attn, kv, page_table, row_pt, sel, *, max_bound: 
     assert lse.dtype == torch.float32 and tuple(lse.shape) == (R, ATTN_HEADS) and lse.is_contiguous()
     if workspace is None:
         workspace = attention_workspace(R, topk, q_attn.device)
+    _on_one_gpu(q_attn, kv, page_table, row_pt, sel, out, lse, workspace)
     prob = make_problem(rows=R, num_pages=kv.shape[0], pt_rows=page_table.shape[0], pt_stride=page_table.shape[1],
                         max_bound=max_bound, topk=topk)
     _check(load_library().indexer_sparse_attention(ctypes.byref(prob), _ptr(q_attn), _ptr(kv), _ptr(page_table),

@@ -298,3 +298,21 @@ def test_binding_rejects_host_tensors_before_any_call(lib):
             fn(q, w, k, ks, pt, rp, rb, max_bound=100)
     with pytest.raises(AssertionError, match="one GPU"):
         fk.indexer_launch_score(q, w, k, ks, pt, rp, rb, max_bound=100, workspace=torch.zeros(256, dtype=torch.uint8))
+    sc = torch.zeros(R, 128)
+    with pytest.raises(AssertionError, match="one GPU"):
+        fk.indexer_topk(sc, rb, max_bound=100)
+    with pytest.raises(AssertionError, match="one GPU"):
+        fk.indexer_launch_select(rb, max_bound=100, scores=sc, workspace=torch.zeros(256, dtype=torch.uint8))
+    with pytest.raises(AssertionError, match="one GPU"):
+        fk.indexer_validate(pt, rp, rb, max_bound=100, num_pages=4)
+    with pytest.raises(AssertionError, match="one GPU"):
+        fk.indexer_write_keys(torch.zeros(R, fk.HEAD_DIM, dtype=torch.bfloat16), k, ks, pt, rp, rb, max_bound=100)
+    with pytest.raises(AssertionError, match="one GPU"):
+        fk.indexer_merge_topk(torch.zeros(R, 2 * 8), torch.zeros(R, 2 * 8, dtype=torch.int32), shards=2, topk=8)
+    sel = torch.zeros(R, 8, dtype=torch.int32)
+    with pytest.raises(AssertionError, match="one GPU"):
+        fk.indexer_shard_candidates(sc, sel, shard=0, shards=2, max_bound=100)
+    with pytest.raises(AssertionError, match="one GPU"):
+        fk.indexer_sparse_attention(torch.zeros(R, fk.ATTN_HEADS, fk.ATTN_DIM, dtype=torch.bfloat16),
+                                    torch.zeros(4, fk.PAGE, fk.ATTN_DIM, dtype=torch.bfloat16), pt, rp, sel,
+                                    max_bound=100, sm_scale=0.1)
