@@ -262,6 +262,46 @@ def indexer_launch(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound, *, max_
 
 
 
+class LaunchPlan:
+    """indexer_launch with its arguments checked and marshalled once, for
+    loops that launch on the same buffers again and again (new contents
+    copied in between, as a serving step does): each call is then one C call
+    on the device's current stream.  The tensors are kept alive by the plan;
+    their shapes, dtypes and storage must not change while it is used.
+    Arguments as for indexer_launch; ``plan()`` returns out_idx."""
+
+    def __init__(self, q, w, k_e4m3, k_scale, page_table, row_pt, row_bound, *, max_bound: int,
+                 topk: int = MAX_TOPK, scores=None, out_idx=None, workspace=None):
+        import torch
+        _check_inputs(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound)
+        R = q.shape[0]
+        if scores is not None:
+            _check_scores(scores, R, max_bound, q.device)
+        sstride = scores.stride(0) if scores is not None else 0
+        self._prob = _problem_from(q, k_e4m3, page_table, max_bound, topk, sstride)
+        if out_idx is None:
+            out_idx = torch.empty((R, topk), dtype=torch.int32, device=q.device)
+        _check_out(out_idx, R, topk, q.device)
+        if workspace is None:
+            workspace = new_workspace(self._prob, scores is None, q.device)
+        _on_one_gpu(q, workspace)
+        self.out_idx = out_idx
+        self._keep = (q, w, k_e4m3, k_scale, page_table, row_pt, row_bound, scores, out_idx, workspace)
+        self._device = q.device
+        self._fn = load_library().indexer_launch
+        vp = ctypes.c_void_p
+        self._args = (ctypes.byref(self._prob),) + tuple(
+            vp(_ptr(t)) for t in (q, w, k_e4m3, k_scale, page_table, row_pt, row_bound, scores, out_idx,
+                                  workspace)) + (ctypes.c_size_t(workspace.numel()),)
+
+    def __call__(self):
+        import torch
+        rc = self._fn(*self._args, torch.cuda.current_stream(self._device).cuda_stream)
+        if rc != 0:
+            _check(rc)
+        return self.out_idx
+
+
 def indexer_launch_score(q, w, k_e4m3, k_scale, page_table, row_pt, row_bound, *, max_bound: int,
                          topk: int = MAX_TOPK, scores=None, workspace):
     """The scoring stage of indexer_launch: scores (into the workspace when

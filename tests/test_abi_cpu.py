@@ -316,3 +316,15 @@ def test_binding_rejects_host_tensors_before_any_call(lib):
         fk.indexer_sparse_attention(torch.zeros(R, fk.ATTN_HEADS, fk.ATTN_DIM, dtype=torch.bfloat16),
                                     torch.zeros(4, fk.PAGE, fk.ATTN_DIM, dtype=torch.bfloat16), pt, rp, sel,
                                     max_bound=100, sm_scale=0.1)
+
+
+def test_launch_plan_rejects_host_tensors(lib):
+    import torch
+    import fp8_key_scoring_amd as fk
+    R = 2
+    args = (torch.zeros(R, fk.HEADS, fk.HEAD_DIM, dtype=torch.bfloat16), torch.zeros(R, fk.HEADS),
+            torch.zeros(4, fk.PAGE, fk.HEAD_DIM, dtype=torch.uint8), torch.zeros(4, fk.PAGE),
+            torch.zeros(1, 4, dtype=torch.int32), torch.zeros(R, dtype=torch.int32),
+            torch.full((R,), 100, dtype=torch.int32))
+    with pytest.raises(AssertionError, match="one GPU"):
+        fk.LaunchPlan(*args, max_bound=100)

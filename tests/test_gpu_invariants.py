@@ -61,6 +61,28 @@ def test_launch_equals_its_two_stages():
             assert np.array_equal(o1, o2.cpu().numpy()), (own, rep)
         assert not ws[:_zero_block_bytes(p.rows)].any(), "counters left non-zero"
 
+def test_launch_plan_follows_new_contents():
+    # a LaunchPlan on fixed buffers: new problem contents copied in between
+    # calls give each problem's own launch, byte for byte (scores too)
+    pa, pb = _prob(26), _prob(27)
+    say("[gpu] launch plan over new contents")
+    da, db = to_device(pa), to_device(pb)
+    assert all(da[n].shape == db[n].shape for n in da)
+    mb = pa.max_bound
+    buf = {n: t.clone() for n, t in da.items()}
+    sc = torch.full((pa.rows, mb), float("nan"), dtype=torch.float32, device="cuda:0")
+    plan = fk.LaunchPlan(**buf, max_bound=mb, topk=pa.topk, scores=sc)
+    for p, d in ((pa, da), (pb, db), (pa, da)):
+        ref_s, ref_o = run_launch(p)
+        for n in buf:
+            buf[n].copy_(d[n])
+        sc.fill_(float("nan"))
+        out = plan()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), ref_o)
+        assert np.array_equal(sc.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+
+
 def test_scores_in_workspace():
     p = _prob(23)
     say("[gpu] scores kept in the workspace")
