@@ -2,7 +2,8 @@
 
 Workload: one request's 4 verify rows over 524,288 paged E4M3 keys (bounds
 n-3..n), 64 heads x 128, page 64, top-2048.  A step is one indexer_launch
-call (through a LaunchPlan: the arguments checked and marshalled once).  Inputs sit in HBM before timing starts; the timed steps rotate over
+call (through a LaunchPlan: the arguments checked and marshalled once).
+Inputs sit in HBM before timing starts; the timed steps rotate over
 several copies of the key pool and page table (together larger than the
 256 MB MALL) so each step streams its keys from HBM.  Before the warmup
 steps the launch runs back to back, untimed, for --settle seconds, so the
